@@ -1,0 +1,171 @@
+/*
+ * msk — speculative-verify MoE layer kernel for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the library. The operation is the verify pass of a
+ * mixture-of-experts decoder described in "Muse Spark Open Ultrafast: Pushing
+ * beyond 1,000 Tokens per second" (LMSYS, Nov 2026; summaries on
+ * newruntime.com, section "What happened", and orcarouter.ai, sections
+ * "Dove si colloca il confine del kernel" and the model paragraph after it):
+ * one resident kernel launch per layer boundary, covering one layer's
+ * attention over a bf16 KV cache, the router (top-k of E experts), the pooler,
+ * the NVFP4 expert SwiGLU, the unpooler, and then the next layer's QKV
+ * projection and KV write.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are device pointers owned by the caller. Weights and KV
+ *    caches are borrowed by msk_load_layer and must outlive the handle; IO
+ *    buffers must stay valid until the enqueued work has finished.
+ *  - Every device pointer must be 16-byte aligned (128-bit loads).
+ *  - The library allocates no device memory: its scratch space is the
+ *    caller's workspace (msk_workspace_bytes). It allocates a few bytes of
+ *    pinned host memory per handle for the device error word.
+ *  - Calls are asynchronous on the given stream (a hipStream_t passed as
+ *    void*; NULL is the default stream) and return once the work is
+ *    enqueued. They enqueue no memset and no allocation, so a caller may
+ *    capture them in a hipGraph. Calls on one handle are not thread-safe.
+ *  - Errors are returned as msk_status; nothing throws or aborts across the
+ *    ABI. msk_last_error() describes the last failure on a handle.
+ *
+ * Weight layouts (row-major, [out][in], the input dim contiguous):
+ *  w_qkv    bf16 [nq*d + 2*nkv*d][H], rows Q (head-major) | K | V
+ *  w_o      bf16 [H][nq*d]
+ *  w_router fp32 [E][H]; b_router fp32 [E] or NULL (added to the logits)
+ *  w_pool   bf16 [P][H];   w_unpool bf16 [H][P]
+ *  g_attn, g_moe bf16 [H]  RMSNorm gains (pre-attention, pre-MoE)
+ *  e_gate_up       [E][2I][P/2]  E2M1 codes, rows gate | up; element 2j of a
+ *                                row in the low nibble of byte j
+ *  e_gate_up_scale [E][2I][P/16] E4M3 (OCP, bias 7) scale per 16 elements
+ *  e_down          [E][P][I/2]   E2M1;  e_down_scale [E][P][I/16] E4M3
+ *  e_tensor_scale  fp32 [E][2]   per-tensor scale of gate_up and of down
+ *  k_cache, v_cache bf16 [max_requests][nkv][kv_capacity][d]
+ * Activations: h_in / h_out fp32 [n_requests * n_tokens][H], request-major.
+ */
+#ifndef MSK_H
+#define MSK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct msk_handle_s* msk_handle;
+
+typedef enum {
+  MSK_OK = 0,
+  MSK_E_INVALID = 1,  /* NULL or out-of-range argument */
+  MSK_E_SHAPE = 2,    /* shapes the kernel does not support */
+  MSK_E_ALIGN = 3,    /* pointer not 16-byte aligned */
+  MSK_E_STATE = 4,    /* layer not loaded, or handle in a failed state */
+  MSK_E_CAPACITY = 5, /* ctx_len + n_tokens > kv_capacity, or too many tokens */
+  MSK_E_HIP = 6,      /* a HIP runtime call failed */
+  MSK_E_TIMEOUT = 7   /* a kernel wait exceeded its spin budget (reported by the next call) */
+} msk_status;
+
+/* msk_config.flags */
+#define MSK_FLAG_NO_NORM 0x1u /* skip both RMSNorms (special-case tests) */
+
+typedef struct {
+  int32_t hidden;        /* H, multiple of 128; nq*d also a multiple of 128 */
+  int32_t n_q_heads;     /* nq */
+  int32_t n_kv_heads;    /* nkv; nq / nkv <= 8 */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t n_experts;     /* E <= 256 */
+  int32_t top_k;         /* k <= 8 */
+  int32_t pool_dim;      /* P, multiple of 128 */
+  int32_t expert_inter;  /* I, multiple of 32 */
+  int32_t n_layers;      /* layers of the step (msk_verify_step) */
+  int32_t max_tokens;    /* verify tokens per request, <= 16 */
+  int32_t max_requests;  /* <= 4 */
+  int32_t kv_capacity;   /* cache rows per (request, kv head) */
+  float rms_eps;
+  uint32_t flags;
+} msk_config;
+
+typedef struct {
+  int32_t window; /* sliding window in keys (including the query's own position); 0 = global */
+  const uint16_t* w_qkv;
+  const uint16_t* w_o;
+  const float* w_router;
+  const float* b_router; /* may be NULL */
+  const uint16_t* w_pool;
+  const uint16_t* w_unpool;
+  const uint16_t* g_attn;
+  const uint16_t* g_moe;
+  const uint8_t* e_gate_up;
+  const uint8_t* e_gate_up_scale;
+  const uint8_t* e_down;
+  const uint8_t* e_down_scale;
+  const float* e_tensor_scale;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+} msk_layer_desc;
+
+/* Optional stage dumps of msk_verify_layer (device pointers, each may be NULL;
+ * NT = n_requests * n_tokens). Used to check stages one by one. */
+typedef struct {
+  float* q;          /* [NT][nq*d]   query rows of the layer */
+  float* k_new;      /* [NT][nkv*d]  new K rows before the bf16 store */
+  float* v_new;      /* [NT][nkv*d]  */
+  float* attn;       /* [NT][nq*d]   attention output */
+  float* h1;         /* [NT][H]      residual after the output projection */
+  float* n2;         /* [NT][H]      fp32 router input */
+  float* logits;     /* [NT][E]      fp32 router logits (bias included) */
+  float* p;          /* [NT][P]      pooled vector */
+  float* acc;        /* [NT][P]      gated expert sum, before the unpooler */
+  int32_t dq_expert; /* expert whose decoded weights are dumped (if selected) */
+  uint16_t* dq_gate_up; /* f16 [2I][P]: E2M1 x E4M3 (tensor scale not applied) */
+  uint16_t* dq_down;    /* f16 [P][I] */
+} msk_debug;
+
+typedef struct {
+  int32_t n_requests;     /* R, 1 .. max_requests */
+  int32_t n_tokens;       /* T tokens per request, 1 .. max_tokens */
+  const int32_t* ctx_len; /* HOST array [R]: prior context length; the tokens
+                             take positions ctx_len[r] .. ctx_len[r] + T - 1 */
+  const float* h_in;      /* device fp32 [R*T][H] */
+  float* h_out;           /* device fp32 [R*T][H] */
+  int32_t* expert_ids;    /* device, may be NULL: [L][R*T][k] (verify_layer: [R*T][k]) */
+  float* gates;           /* device, may be NULL: same shape as expert_ids */
+  const msk_debug* debug; /* HOST struct, may be NULL; honoured by msk_verify_layer */
+} msk_io;
+
+/* Bytes of device workspace a handle needs for this configuration; 0 if the
+ * configuration is invalid. */
+size_t msk_workspace_bytes(const msk_config* cfg);
+
+/* Create a handle. workspace: device memory of at least msk_workspace_bytes,
+ * owned by the caller, 256-byte aligned, kept until msk_destroy. The call
+ * writes the workspace's schedule tables (synchronously) and uses the current
+ * HIP device. */
+msk_status msk_create(const msk_config* cfg, void* workspace, size_t bytes, msk_handle* out);
+
+/* Register layer `layer` (0 .. n_layers-1). Pointers are borrowed. */
+msk_status msk_load_layer(msk_handle h, int32_t layer, const msk_layer_desc* desc);
+
+/* One standalone layer: its own RMSNorm + QKV projection + KV write at
+ * positions ctx_len[r] .., attention, output projection, router, pooler,
+ * experts, unpooler. h_out = the layer's output residual. One kernel launch
+ * (plus one tiny counter-reset launch). */
+msk_status msk_verify_layer(msk_handle h, int32_t layer, const msk_io* io, void* stream);
+
+/* The whole verify step over layers 0 .. n_layers-1: one resident kernel per
+ * layer boundary. Launch L runs layer L's attention through its unpooler,
+ * then layer L+1's RMSNorm, QKV projection and KV write; the first launch
+ * also runs layer 0's QKV and KV write first. expert_ids/gates, if given,
+ * receive every layer's routing. */
+msk_status msk_verify_step(msk_handle h, const msk_io* io, void* stream);
+
+/* Release the handle (the workspace stays the caller's). */
+msk_status msk_destroy(msk_handle h);
+
+/* Description of the last error on h (or of the last msk_create failure when
+ * h is NULL). Never NULL. */
+const char* msk_last_error(msk_handle h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSK_H */

@@ -1,0 +1,453 @@
+// Host side of the msk C ABI (include/msk.h): argument validation, workspace
+// carving, the static schedules of the dense projections, and the launches of
+// the layer kernel (msk_layer.hip).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/msk.h"
+#include "msk_internal.h"
+
+namespace {
+
+constexpr int kMaxGrid = 256;  // workgroups per launch at most (one per compute unit)
+
+struct Layout {
+  size_t bar, sched, h1, ssq1, ssq2, hbuf0, hbuf1, qpart, apart, attn, logits, ppart, abuf, accpart, hist;
+  size_t total;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct SchedHost {
+  std::vector<msk::Unit> units;
+  std::vector<int32_t> off;
+  int64_t max_load = 0;
+};
+
+struct TileSpec {
+  int tile;
+  int klen;
+  bool splittable;
+};
+
+// Longest-processing-time assignment of units to G workgroups; splittable
+// tiles are cut into `slices` equal k ranges (slot = slice index).
+SchedHost build_sched(const std::vector<TileSpec>& tiles, int slices, int G) {
+  std::vector<msk::Unit> all;
+  for (const TileSpec& t : tiles) {
+    if (t.splittable && slices > 1) {
+      int kl = t.klen / slices;
+      for (int s = 0; s < slices; ++s) all.push_back({t.tile, s * kl, kl, s});
+    } else {
+      all.push_back({t.tile, 0, t.klen, 0});
+    }
+  }
+  std::stable_sort(all.begin(), all.end(), [](const msk::Unit& a, const msk::Unit& b) { return a.klen > b.klen; });
+  std::vector<std::vector<msk::Unit>> per(G);
+  std::vector<int64_t> load(G, 0);
+  for (const msk::Unit& u : all) {
+    int best = 0;
+    for (int g = 1; g < G; ++g)
+      if (load[g] < load[best]) best = g;
+    per[best].push_back(u);
+    load[best] += u.klen;
+  }
+  SchedHost sh;
+  sh.off.push_back(0);
+  for (int g = 0; g < G; ++g) {
+    for (const msk::Unit& u : per[g]) sh.units.push_back(u);
+    sh.off.push_back((int32_t)sh.units.size());
+    sh.max_load = std::max(sh.max_load, load[g]);
+  }
+  return sh;
+}
+
+// Best slice count in {1, 2, 4} (fewest slices among the lowest max load).
+SchedHost build_sched_best(const std::vector<TileSpec>& tiles, int K, int G, int* slices_out) {
+  SchedHost best;
+  int best_s = 1;
+  for (int s : {1, 2, 4}) {
+    if (K % (s * msk::kSubK) != 0) continue;
+    if (K / s > msk::kSubK * msk::kWaves * msk::kMaxSubPerWave) continue;
+    SchedHost sh = build_sched(tiles, s, G);
+    if (best.off.empty() || sh.max_load < best.max_load) {
+      best = std::move(sh);
+      best_s = s;
+    }
+  }
+  *slices_out = best_s;
+  return best;
+}
+
+}  // namespace
+
+struct msk_handle_s {
+  msk_config cfg;
+  int grid = 0;
+  uint8_t* ws = nullptr;
+  size_t ws_bytes = 0;
+  Layout lay{};
+  std::vector<msk_layer_desc> layers;
+  std::vector<bool> loaded;
+  int q_slices = 1, p_slices = 1;
+  msk::Sched s_qkv{}, s_oproj{}, s_pool{}, s_unpool{};
+  int32_t* err_host = nullptr;
+  std::string last_error;
+};
+
+namespace {
+
+thread_local std::string g_create_error;
+
+msk_status fail(msk_handle h, msk_status st, const std::string& msg) {
+  if (h) h->last_error = msg;
+  else g_create_error = msg;
+  return st;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks; returns an empty string when the configuration is supported.
+std::string check_config(const msk_config* c) {
+  if (!c) return "config is NULL";
+  const int Dq = c->n_q_heads * c->head_dim;
+  if (c->hidden <= 0 || c->hidden % 128 != 0 || c->hidden > 4096) return "hidden must be a positive multiple of 128, <= 4096";
+  if (c->head_dim != 64 && c->head_dim != 128) return "head_dim must be 64 or 128";
+  if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads != 0) return "n_q_heads must be a multiple of n_kv_heads";
+  if (c->n_q_heads / c->n_kv_heads > msk::kWaves) return "at most 8 query heads per kv head";
+  if (Dq % 128 != 0 || Dq > 4096) return "n_q_heads*head_dim must be a multiple of 128, <= 4096";
+  if (c->n_experts <= 0 || c->n_experts > msk::kMaxE) return "n_experts must be in 1..256";
+  if (c->top_k <= 0 || c->top_k > msk::kMaxK || c->top_k > c->n_experts) return "top_k must be in 1..min(8, n_experts)";
+  if (c->pool_dim <= 0 || c->pool_dim % 128 != 0 || c->pool_dim > 2048) return "pool_dim must be a positive multiple of 128, <= 2048";
+  if (c->expert_inter <= 0 || c->expert_inter % 32 != 0 || c->expert_inter > 1024) return "expert_inter must be a positive multiple of 32, <= 1024";
+  if (c->n_layers <= 0) return "n_layers must be positive";
+  if (c->max_tokens <= 0 || c->max_tokens > msk::kMaxTok) return "max_tokens must be in 1..16";
+  if (c->max_requests <= 0 || c->max_requests > msk::kMaxReq) return "max_requests must be in 1..4";
+  if (c->max_tokens * c->max_requests > msk::kMaxTok) return "max_tokens*max_requests must be <= 16";
+  if (c->kv_capacity <= 0) return "kv_capacity must be positive";
+  if (!(c->rms_eps >= 0.0f)) return "rms_eps must be >= 0";
+  return std::string();
+}
+
+Layout make_layout(const msk_config* c, int G) {
+  const size_t NT = (size_t)c->max_tokens * c->max_requests;
+  const size_t H = c->hidden, Dq = (size_t)c->n_q_heads * c->head_dim, P = c->pool_dim, I = c->expert_inter;
+  const size_t E = c->n_experts, K = c->top_k;
+  const size_t nsel = std::min(E, NT * K);
+  const size_t parts = std::max<size_t>(1, (size_t)G / (P / 16));
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.bar = take(256);
+  // schedule tables: units of 4 schedules + offsets (generous bound)
+  const size_t max_units = 4 * ((H / 16) * 4 + (Dq + 2 * c->n_kv_heads * c->head_dim) / 16 * 4 + (P / 16) * 4) + 64;
+  L.sched = take(max_units * sizeof(msk::Unit) + 4 * (G + 1) * sizeof(int32_t));
+  L.h1 = take(NT * H * 4);
+  L.ssq1 = take((H / 16) * NT * 4);
+  L.ssq2 = take((H / 16) * NT * 4);
+  L.hbuf0 = take(NT * H * 4);
+  L.hbuf1 = take(NT * H * 4);
+  L.qpart = take(4 * NT * Dq * 4);
+  L.apart = take((size_t)G * msk::kWaves * msk::kMaxTok * (c->head_dim + 2) * 4);
+  L.attn = take(NT * Dq * 2);
+  L.logits = take(NT * E * 4);
+  L.ppart = take(4 * NT * P * 4);
+  L.abuf = take(nsel * NT * I * 2);
+  L.accpart = take(parts * NT * P * 4);
+  L.hist = take((size_t)c->n_layers * E * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" size_t msk_workspace_bytes(const msk_config* cfg) {
+  if (!check_config(cfg).empty()) return 0;
+  return make_layout(cfg, kMaxGrid).total;
+}
+
+extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t bytes, msk_handle* out) {
+  if (!out) return fail(nullptr, MSK_E_INVALID, "out is NULL");
+  *out = nullptr;
+  std::string why = check_config(cfg);
+  if (!why.empty()) return fail(nullptr, MSK_E_SHAPE, why);
+  if (!workspace) return fail(nullptr, MSK_E_INVALID, "workspace is NULL");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(nullptr, MSK_E_ALIGN, "workspace must be 256-byte aligned");
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return fail(nullptr, MSK_E_HIP, "no HIP device");
+  const int G = std::min(prop.multiProcessorCount, kMaxGrid);
+  Layout lay = make_layout(cfg, kMaxGrid);
+  if (bytes < lay.total) return fail(nullptr, MSK_E_CAPACITY, "workspace smaller than msk_workspace_bytes");
+
+  msk_handle h = new (std::nothrow) msk_handle_s();
+  if (!h) return fail(nullptr, MSK_E_INVALID, "out of host memory");
+  h->cfg = *cfg;
+  h->grid = G;
+  h->ws = (uint8_t*)workspace;
+  h->ws_bytes = bytes;
+  h->lay = lay;
+  h->layers.resize(cfg->n_layers);
+  h->loaded.assign(cfg->n_layers, false);
+
+  // dense schedules
+  const int H = cfg->hidden, Dq = cfg->n_q_heads * cfg->head_dim, Dkv = cfg->n_kv_heads * cfg->head_dim;
+  const int P = cfg->pool_dim;
+  std::vector<TileSpec> t_qkv, t_oproj, t_pool, t_unpool;
+  for (int t = 0; t < (Dq + 2 * Dkv) / 16; ++t) t_qkv.push_back({t, H, t * 16 < Dq});
+  for (int t = 0; t < H / 16; ++t) t_oproj.push_back({t, Dq, false});
+  for (int t = 0; t < P / 16; ++t) t_pool.push_back({t, H, true});
+  for (int t = 0; t < H / 16; ++t) t_unpool.push_back({t, P, false});
+  SchedHost sq = build_sched_best(t_qkv, H, G, &h->q_slices);
+  SchedHost so = build_sched(t_oproj, 1, G);
+  SchedHost sp = build_sched_best(t_pool, H, G, &h->p_slices);
+  SchedHost su = build_sched(t_unpool, 1, G);
+
+  std::vector<uint8_t> blob;
+  auto put = [&](const SchedHost& s, msk::Sched& dst) {
+    size_t at = align_up(blob.size(), 16);
+    blob.resize(at + s.units.size() * sizeof(msk::Unit));
+    if (!s.units.empty()) memcpy(blob.data() + at, s.units.data(), s.units.size() * sizeof(msk::Unit));
+    size_t at2 = align_up(blob.size(), 16);
+    blob.resize(at2 + s.off.size() * sizeof(int32_t));
+    memcpy(blob.data() + at2, s.off.data(), s.off.size() * sizeof(int32_t));
+    dst.units = reinterpret_cast<const msk::Unit*>(h->ws + lay.sched + at);
+    dst.off = reinterpret_cast<const int32_t*>(h->ws + lay.sched + at2);
+  };
+  put(sq, h->s_qkv);
+  put(so, h->s_oproj);
+  put(sp, h->s_pool);
+  put(su, h->s_unpool);
+  if (blob.size() > lay.h1 - lay.sched) {
+    delete h;
+    return fail(nullptr, MSK_E_CAPACITY, "schedule tables exceed their workspace region");
+  }
+  if (hipMemcpy(h->ws + lay.sched, blob.data(), blob.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    delete h;
+    return fail(nullptr, MSK_E_HIP, "hipMemcpy of the schedule tables failed");
+  }
+  // zero the barrier word, error word and routing histogram once
+  std::vector<uint8_t> zeros(std::max<size_t>(256, (size_t)cfg->n_layers * cfg->n_experts * 4), 0);
+  if (hipMemcpy(h->ws + lay.bar, zeros.data(), 256, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(h->ws + lay.hist, zeros.data(), (size_t)cfg->n_layers * cfg->n_experts * 4, hipMemcpyHostToDevice) != hipSuccess) {
+    delete h;
+    return fail(nullptr, MSK_E_HIP, "hipMemcpy of the workspace header failed");
+  }
+  if (hipHostMalloc((void**)&h->err_host, 256, hipHostMallocDefault) != hipSuccess) {
+    delete h;
+    return fail(nullptr, MSK_E_HIP, "hipHostMalloc of the error word failed");
+  }
+  *h->err_host = 0;
+  *out = h;
+  return MSK_OK;
+}
+
+extern "C" msk_status msk_load_layer(msk_handle h, int32_t layer, const msk_layer_desc* d) {
+  if (!h) return fail(nullptr, MSK_E_INVALID, "handle is NULL");
+  if (!d) return fail(h, MSK_E_INVALID, "desc is NULL");
+  if (layer < 0 || layer >= h->cfg.n_layers) return fail(h, MSK_E_INVALID, "layer out of range");
+  if (d->window < 0) return fail(h, MSK_E_INVALID, "window must be >= 0");
+  const void* req[] = {d->w_qkv, d->w_o, d->w_router, d->w_pool, d->w_unpool, d->g_attn, d->g_moe,
+                       d->e_gate_up, d->e_gate_up_scale, d->e_down, d->e_down_scale, d->e_tensor_scale,
+                       d->k_cache, d->v_cache};
+  for (const void* p : req) {
+    if (!p) return fail(h, MSK_E_INVALID, "a required layer pointer is NULL");
+    if (!aligned16(p)) return fail(h, MSK_E_ALIGN, "layer pointers must be 16-byte aligned");
+  }
+  if (d->b_router && !aligned16(d->b_router)) return fail(h, MSK_E_ALIGN, "b_router must be 16-byte aligned");
+  h->layers[layer] = *d;
+  h->loaded[layer] = true;
+  return MSK_OK;
+}
+
+namespace {
+
+msk::LayerW to_w(const msk_layer_desc& d) {
+  msk::LayerW w;
+  w.w_qkv = d.w_qkv;
+  w.w_o = d.w_o;
+  w.w_router = d.w_router;
+  w.b_router = d.b_router;
+  w.w_pool = d.w_pool;
+  w.w_unpool = d.w_unpool;
+  w.g_attn = d.g_attn;
+  w.g_moe = d.g_moe;
+  w.e_gu = d.e_gate_up;
+  w.e_gu_sc = d.e_gate_up_scale;
+  w.e_dn = d.e_down;
+  w.e_dn_sc = d.e_down_scale;
+  w.e_ts = d.e_tensor_scale;
+  w.k_cache = d.k_cache;
+  w.v_cache = d.v_cache;
+  w.window = d.window;
+  return w;
+}
+
+msk_status check_io(msk_handle h, const msk_io* io) {
+  if (!io) return fail(h, MSK_E_INVALID, "io is NULL");
+  const msk_config& c = h->cfg;
+  if (io->n_requests < 1 || io->n_requests > c.max_requests) return fail(h, MSK_E_INVALID, "n_requests out of range");
+  if (io->n_tokens < 1 || io->n_tokens > c.max_tokens) return fail(h, MSK_E_INVALID, "n_tokens out of range");
+  if (!io->ctx_len) return fail(h, MSK_E_INVALID, "ctx_len is NULL");
+  for (int r = 0; r < io->n_requests; ++r) {
+    if (io->ctx_len[r] < 0) return fail(h, MSK_E_INVALID, "ctx_len must be >= 0");
+    if ((int64_t)io->ctx_len[r] + io->n_tokens > c.kv_capacity) return fail(h, MSK_E_CAPACITY, "ctx_len + n_tokens exceeds kv_capacity");
+  }
+  if (!io->h_in || !io->h_out) return fail(h, MSK_E_INVALID, "h_in and h_out are required");
+  if (!aligned16(io->h_in) || !aligned16(io->h_out)) return fail(h, MSK_E_ALIGN, "h_in/h_out must be 16-byte aligned");
+  if ((io->expert_ids && !aligned16(io->expert_ids)) || (io->gates && !aligned16(io->gates)))
+    return fail(h, MSK_E_ALIGN, "expert_ids/gates must be 16-byte aligned");
+  if (*h->err_host != 0) {
+    int e = *h->err_host;
+    *h->err_host = 0;
+    char buf[96];
+    snprintf(buf, sizeof buf, "a previous launch reported device error %d (spin budget exceeded)", e);
+    return fail(h, MSK_E_TIMEOUT, buf);
+  }
+  return MSK_OK;
+}
+
+msk::Params base_params(msk_handle h, const msk_io* io) {
+  const msk_config& c = h->cfg;
+  const Layout& L = h->lay;
+  msk::Params p;
+  memset(&p, 0, sizeof p);
+  p.H = c.hidden;
+  p.nq = c.n_q_heads;
+  p.nkv = c.n_kv_heads;
+  p.d = c.head_dim;
+  p.E = c.n_experts;
+  p.topk = c.top_k;
+  p.P = c.pool_dim;
+  p.I = c.expert_inter;
+  p.R = io->n_requests;
+  p.T = io->n_tokens;
+  p.NT = io->n_requests * io->n_tokens;
+  p.cap = c.kv_capacity;
+  p.use_norm = (c.flags & MSK_FLAG_NO_NORM) ? 0 : 1;
+  p.eps = c.rms_eps;
+  for (int r = 0; r < io->n_requests; ++r) p.ctx[r] = io->ctx_len[r];
+  p.q_slices = h->q_slices;
+  p.p_slices = h->p_slices;
+  uint8_t* ws = h->ws;
+  p.bar = reinterpret_cast<uint32_t*>(ws + L.bar);
+  p.err = reinterpret_cast<int32_t*>(ws + L.bar + 64);
+  p.h1 = reinterpret_cast<float*>(ws + L.h1);
+  p.ssq1 = reinterpret_cast<float*>(ws + L.ssq1);
+  p.ssq2 = reinterpret_cast<float*>(ws + L.ssq2);
+  p.qpart = reinterpret_cast<float*>(ws + L.qpart);
+  p.apart = reinterpret_cast<float*>(ws + L.apart);
+  p.attn = reinterpret_cast<uint16_t*>(ws + L.attn);
+  p.logits = reinterpret_cast<float*>(ws + L.logits);
+  p.ppart = reinterpret_cast<float*>(ws + L.ppart);
+  p.abuf = reinterpret_cast<uint16_t*>(ws + L.abuf);
+  p.accpart = reinterpret_cast<float*>(ws + L.accpart);
+  p.hist = reinterpret_cast<int32_t*>(ws + L.hist);
+  p.s_qkv_own = h->s_qkv;
+  p.s_qkv_next = h->s_qkv;
+  p.s_oproj = h->s_oproj;
+  p.s_pool = h->s_pool;
+  p.s_unpool = h->s_unpool;
+  return p;
+}
+
+int barriers_of(uint32_t mode) {
+  int n = 6;
+  if (mode & msk::kModeQkvOwn) n += 1;
+  if (mode & msk::kModeQkvNext) n += 1;
+  return n;
+}
+
+msk_status finish(msk_handle h, hipStream_t s) {
+  const Layout& L = h->lay;
+  if (hipMemcpyAsync(h->err_host, h->ws + L.bar + 64, 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return fail(h, MSK_E_HIP, "hipMemcpyAsync of the error word failed");
+  return MSK_OK;
+}
+
+}  // namespace
+
+extern "C" msk_status msk_verify_layer(msk_handle h, int32_t layer, const msk_io* io, void* stream) {
+  if (!h) return fail(nullptr, MSK_E_INVALID, "handle is NULL");
+  if (layer < 0 || layer >= h->cfg.n_layers) return fail(h, MSK_E_INVALID, "layer out of range");
+  if (!h->loaded[layer]) return fail(h, MSK_E_STATE, "layer not loaded");
+  msk_status st = check_io(h, io);
+  if (st != MSK_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  msk::Params p = base_params(h, io);
+  p.mode = msk::kModeQkvOwn;
+  p.layer = layer;
+  p.bar_base = 0;
+  p.cur = to_w(h->layers[layer]);
+  p.nxt = p.cur;
+  p.h_in = io->h_in;
+  p.h_out = io->h_out;
+  p.out_ids = io->expert_ids;
+  p.out_gates = io->gates;
+  bool debug = false;
+  if (io->debug) {
+    const msk_debug& d = *io->debug;
+    p.dbg = msk::Debug{d.q, d.k_new, d.v_new, d.attn, d.h1, d.n2, d.logits, d.p, d.acc,
+                       d.dq_expert, d.dq_gate_up, d.dq_down};
+    debug = true;
+  }
+  if (msk_launch_reset(p.bar, p.err, s) != hipSuccess) return fail(h, MSK_E_HIP, "reset launch failed");
+  hipError_t e = msk_launch_layer(p, h->grid, debug, s);
+  if (e != hipSuccess) return fail(h, MSK_E_HIP, std::string("layer launch failed: ") + hipGetErrorString(e));
+  return finish(h, s);
+}
+
+extern "C" msk_status msk_verify_step(msk_handle h, const msk_io* io, void* stream) {
+  if (!h) return fail(nullptr, MSK_E_INVALID, "handle is NULL");
+  for (int l = 0; l < h->cfg.n_layers; ++l)
+    if (!h->loaded[l]) return fail(h, MSK_E_STATE, "not every layer is loaded");
+  msk_status st = check_io(h, io);
+  if (st != MSK_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const Layout& L = h->lay;
+  const int n = h->cfg.n_layers;
+  const int NT = io->n_requests * io->n_tokens;
+  float* hb[2] = {reinterpret_cast<float*>(h->ws + L.hbuf0), reinterpret_cast<float*>(h->ws + L.hbuf1)};
+  if (msk_launch_reset(reinterpret_cast<uint32_t*>(h->ws + L.bar), reinterpret_cast<int32_t*>(h->ws + L.bar + 64), s) != hipSuccess)
+    return fail(h, MSK_E_HIP, "reset launch failed");
+  uint32_t base = 0;
+  for (int l = 0; l < n; ++l) {
+    msk::Params p = base_params(h, io);
+    p.mode = (l == 0 ? msk::kModeQkvOwn : 0u) | (l + 1 < n ? msk::kModeQkvNext : 0u);
+    p.layer = l;
+    p.bar_base = base;
+    p.cur = to_w(h->layers[l]);
+    p.nxt = (l + 1 < n) ? to_w(h->layers[l + 1]) : p.cur;
+    p.h_in = (l == 0) ? io->h_in : hb[(l - 1) & 1];
+    p.h_out = (l == n - 1) ? io->h_out : hb[l & 1];
+    p.out_ids = io->expert_ids ? io->expert_ids + (size_t)l * NT * h->cfg.top_k : nullptr;
+    p.out_gates = io->gates ? io->gates + (size_t)l * NT * h->cfg.top_k : nullptr;
+    hipError_t e = msk_launch_layer(p, h->grid, false, s);
+    if (e != hipSuccess) return fail(h, MSK_E_HIP, std::string("layer launch failed: ") + hipGetErrorString(e));
+    base += barriers_of(p.mode);
+  }
+  return finish(h, s);
+}
+
+extern "C" msk_status msk_destroy(msk_handle h) {
+  if (!h) return fail(nullptr, MSK_E_INVALID, "handle is NULL");
+  if (h->err_host) (void)hipHostFree(h->err_host);
+  delete h;
+  return MSK_OK;
+}
+
+extern "C" const char* msk_last_error(msk_handle h) {
+  if (!h) return g_create_error.c_str();
+  return h->last_error.c_str();
+}

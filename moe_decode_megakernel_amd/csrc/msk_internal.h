@@ -1,0 +1,112 @@
+// Internal definitions shared by the host side (msk_api.cpp) and the layer
+// kernel (msk_layer.hip) of libmsk. Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace msk {
+
+constexpr int kWaves = 8;                 // waves per workgroup
+constexpr int kThreads = kWaves * 64;     // threads per workgroup
+constexpr int kMaxReq = 4;
+constexpr int kMaxTok = 16;               // tokens per launch handled as one 16-row MFMA tile
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 8;
+constexpr int kMaxHeadDim = 128;
+constexpr int kSubK = 128;                // dense k per wave sub-unit (4 MFMA steps of 32)
+constexpr int kMaxSubPerWave = 4;         // sub-units per wave per unit (unit k <= 4096)
+constexpr int kAttnChunk = 64;            // keys per attention chunk in LDS
+
+// Launch modes (bit set).
+enum : uint32_t {
+  kModeQkvOwn = 1u,   // first phase: QKV projection + KV write of the launch's own layer
+  kModeQkvNext = 2u,  // last phase: QKV projection + KV write of the next layer
+};
+
+// Phase-work unit of a dense (bf16) projection: rows [tile*16, tile*16+16), k in [k0, k0+klen).
+struct Unit {
+  int32_t tile, k0, klen, slot;
+};
+
+struct LayerW {
+  const uint16_t* w_qkv;
+  const uint16_t* w_o;
+  const float* w_router;
+  const float* b_router;
+  const uint16_t* w_pool;
+  const uint16_t* w_unpool;
+  const uint16_t* g_attn;
+  const uint16_t* g_moe;
+  const uint8_t* e_gu;
+  const uint8_t* e_gu_sc;
+  const uint8_t* e_dn;
+  const uint8_t* e_dn_sc;
+  const float* e_ts;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int32_t window;
+};
+
+struct Debug {
+  float* q;
+  float* k_new;
+  float* v_new;
+  float* attn;
+  float* h1;
+  float* n2;
+  float* logits;
+  float* p;
+  float* acc;
+  int32_t dq_expert;
+  uint16_t* dq_gu;
+  uint16_t* dq_dn;
+};
+
+// Schedules of the dense phases (CSR over workgroups), built once per handle.
+struct Sched {
+  const Unit* units;
+  const int32_t* off;  // [G + 1]
+};
+
+struct Params {
+  // shapes
+  int32_t H, nq, nkv, d, E, topk, P, I;
+  int32_t R, T, NT, cap;
+  int32_t use_norm;
+  float eps;
+  int32_t ctx[kMaxReq];
+  int32_t q_slices, p_slices;
+  uint32_t mode;
+  int32_t layer;          // layer whose attention .. unpooler this launch runs
+  uint32_t bar_base;      // barriers completed in this call before this launch
+  LayerW cur, nxt;        // nxt: layer whose QKV / KV write ends the launch
+  const float* h_in;      // residual entering `layer`
+  float* h_out;           // residual leaving `layer`
+  // workspace
+  uint32_t* bar;          // grid barrier counter
+  int32_t* err;           // device error word
+  float* h1;              // [NT][H]
+  float* ssq1;            // [H/16][NT] partial sums of squares of h1
+  float* ssq2;            // [H/16][NT] of the launch's output residual
+  float* qpart;           // [q_slices][NT][Dq]
+  float* apart;           // attention partials
+  uint16_t* attn;         // fp16 [NT][Dq] merged attention output
+  float* logits;          // [NT][E]
+  float* ppart;           // [p_slices][NT][P]
+  uint16_t* abuf;         // f16 [n_sel_max][NT][I]
+  float* accpart;         // [parts][NT][P]
+  int32_t* hist;          // [n_layers][E] selection counts
+  Sched s_qkv_own, s_qkv_next, s_oproj, s_pool, s_unpool;
+  // outputs
+  int32_t* out_ids;       // [NT][k] or NULL
+  float* out_gates;
+  Debug dbg;
+};
+
+}  // namespace msk
+
+// Launchers implemented in msk_layer.hip.
+hipError_t msk_launch_layer(const msk::Params& p, int grid, bool debug, hipStream_t s);
+hipError_t msk_launch_reset(uint32_t* bar, int32_t* err, hipStream_t s);

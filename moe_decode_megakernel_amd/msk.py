@@ -1,0 +1,201 @@
+"""Thin ctypes binding of libmsk.so (include/msk.h): the same entry points
+under the same names, plus helpers that marshal torch tensors into the ABI
+structs. All compute runs in the library's HIP kernels; there is no fallback.
+"""
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmsk.so")
+
+i32, u32, f32, vp = ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_void_p
+
+MSK_OK, MSK_E_INVALID, MSK_E_SHAPE, MSK_E_ALIGN, MSK_E_STATE, MSK_E_CAPACITY, MSK_E_HIP, MSK_E_TIMEOUT = range(8)
+STATUS_NAMES = ["MSK_OK", "MSK_E_INVALID", "MSK_E_SHAPE", "MSK_E_ALIGN", "MSK_E_STATE",
+                "MSK_E_CAPACITY", "MSK_E_HIP", "MSK_E_TIMEOUT"]
+MSK_FLAG_NO_NORM = 0x1
+
+EXPORTS = ("msk_workspace_bytes", "msk_create", "msk_load_layer", "msk_verify_layer",
+           "msk_verify_step", "msk_destroy", "msk_last_error")
+
+
+class msk_config(ctypes.Structure):
+    _fields_ = [("hidden", i32), ("n_q_heads", i32), ("n_kv_heads", i32), ("head_dim", i32),
+                ("n_experts", i32), ("top_k", i32), ("pool_dim", i32), ("expert_inter", i32),
+                ("n_layers", i32), ("max_tokens", i32), ("max_requests", i32), ("kv_capacity", i32),
+                ("rms_eps", f32), ("flags", u32)]
+
+
+LAYER_PTRS = ("w_qkv", "w_o", "w_router", "b_router", "w_pool", "w_unpool", "g_attn", "g_moe",
+              "e_gate_up", "e_gate_up_scale", "e_down", "e_down_scale", "e_tensor_scale",
+              "k_cache", "v_cache")
+
+
+class msk_layer_desc(ctypes.Structure):
+    _fields_ = [("window", i32)] + [(n, vp) for n in LAYER_PTRS]
+
+
+DEBUG_PTRS = ("q", "k_new", "v_new", "attn", "h1", "n2", "logits", "p", "acc")
+
+
+class msk_debug(ctypes.Structure):
+    _fields_ = [(n, vp) for n in DEBUG_PTRS] + [("dq_expert", i32), ("dq_gate_up", vp), ("dq_down", vp)]
+
+
+class msk_io(ctypes.Structure):
+    _fields_ = [("n_requests", i32), ("n_tokens", i32), ("ctx_len", ctypes.POINTER(i32)),
+                ("h_in", vp), ("h_out", vp), ("expert_ids", vp), ("gates", vp),
+                ("debug", ctypes.POINTER(msk_debug))]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmsk.so; raises if the HIP library has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with moe_decode_megakernel_amd/build.py "
+                               "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.msk_workspace_bytes.argtypes = [ctypes.POINTER(msk_config)]
+        L.msk_workspace_bytes.restype = ctypes.c_size_t
+        L.msk_create.argtypes = [ctypes.POINTER(msk_config), vp, ctypes.c_size_t, ctypes.POINTER(vp)]
+        L.msk_create.restype = i32
+        L.msk_load_layer.argtypes = [vp, i32, ctypes.POINTER(msk_layer_desc)]
+        L.msk_load_layer.restype = i32
+        L.msk_verify_layer.argtypes = [vp, i32, ctypes.POINTER(msk_io), vp]
+        L.msk_verify_layer.restype = i32
+        L.msk_verify_step.argtypes = [vp, ctypes.POINTER(msk_io), vp]
+        L.msk_verify_step.restype = i32
+        L.msk_destroy.argtypes = [vp]
+        L.msk_destroy.restype = i32
+        L.msk_last_error.argtypes = [vp]
+        L.msk_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+class MskError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS_NAMES[status] if 0 <= status < 8 else status}: {msg}")
+        self.status = status
+
+
+# --- the C entry points under their own names -------------------------------
+def msk_workspace_bytes(cfg: msk_config) -> int:
+    return lib().msk_workspace_bytes(ctypes.byref(cfg))
+
+
+def msk_create(cfg: msk_config, workspace_ptr: int, nbytes: int):
+    h = vp()
+    st = lib().msk_create(ctypes.byref(cfg), vp(workspace_ptr), nbytes, ctypes.byref(h))
+    if st != MSK_OK:
+        raise MskError(st, msk_last_error(None))
+    return h
+
+
+def msk_load_layer(h, layer: int, desc: msk_layer_desc) -> int:
+    return lib().msk_load_layer(h, layer, ctypes.byref(desc))
+
+
+def msk_verify_layer(h, layer: int, io: msk_io, stream: int) -> int:
+    return lib().msk_verify_layer(h, layer, ctypes.byref(io), vp(stream))
+
+
+def msk_verify_step(h, io: msk_io, stream: int) -> int:
+    return lib().msk_verify_step(h, ctypes.byref(io), vp(stream))
+
+
+def msk_destroy(h) -> int:
+    return lib().msk_destroy(h)
+
+
+def msk_last_error(h) -> str:
+    s = lib().msk_last_error(h)
+    return s.decode() if s else ""
+
+
+# --- marshalling helpers (torch tensors -> ABI structs) ----------------------
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def make_config(w, n_layers=None, max_tokens=None, max_requests=None, flags=0) -> msk_config:
+    return msk_config(hidden=w.H, n_q_heads=w.nq, n_kv_heads=w.nkv, head_dim=w.d, n_experts=w.E,
+                      top_k=w.k, pool_dim=w.P, expert_inter=w.I,
+                      n_layers=w.n_layers if n_layers is None else n_layers,
+                      max_tokens=w.T if max_tokens is None else max_tokens,
+                      max_requests=w.R if max_requests is None else max_requests,
+                      kv_capacity=w.cap, rms_eps=w.eps, flags=flags)
+
+
+def make_layer_desc(t: Dict, window: int) -> msk_layer_desc:
+    d = msk_layer_desc(window=window)
+    for n in LAYER_PTRS:
+        setattr(d, n, _ptr(t.get(n)))
+    return d
+
+
+def make_io(n_requests, n_tokens, ctx: Sequence[int], h_in, h_out, expert_ids=None, gates=None,
+            debug: Optional[msk_debug] = None):
+    ctx_arr = (i32 * len(ctx))(*ctx)
+    io = msk_io(n_requests=n_requests, n_tokens=n_tokens, ctx_len=ctypes.cast(ctx_arr, ctypes.POINTER(i32)),
+                h_in=_ptr(h_in), h_out=_ptr(h_out), expert_ids=_ptr(expert_ids), gates=_ptr(gates),
+                debug=ctypes.pointer(debug) if debug is not None else None)
+    io._keep = (ctx_arr, debug)
+    return io
+
+
+def make_debug(t: Dict, dq_expert: int = -1) -> msk_debug:
+    d = msk_debug(dq_expert=dq_expert, dq_gate_up=_ptr(t.get("dq_gate_up")), dq_down=_ptr(t.get("dq_down")))
+    for n in DEBUG_PTRS:
+        setattr(d, n, _ptr(t.get(n)))
+    return d
+
+
+class Handle:
+    """Owns a workspace tensor and a library handle (convenience wrapper)."""
+
+    def __init__(self, cfg: msk_config, device="cuda"):
+        import torch
+        self.cfg = cfg
+        n = msk_workspace_bytes(cfg)
+        if n == 0:
+            raise MskError(MSK_E_SHAPE, "configuration rejected by msk_workspace_bytes")
+        self.workspace = torch.empty(n + 256, dtype=torch.uint8, device=device)
+        base = self.workspace.data_ptr()
+        self.ws_ptr = (base + 255) // 256 * 256
+        self.h = msk_create(cfg, self.ws_ptr, n)
+        self.layers = {}
+
+    def check(self, st):
+        if st != MSK_OK:
+            raise MskError(st, msk_last_error(self.h))
+
+    def load_layer(self, layer, tensors: Dict, window: int):
+        self.layers[layer] = tensors
+        self.check(msk_load_layer(self.h, layer, make_layer_desc(tensors, window)))
+
+    def verify_layer(self, layer, io, stream=None):
+        import torch
+        s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        self.check(msk_verify_layer(self.h, layer, io, s))
+
+    def verify_step(self, io, stream=None):
+        import torch
+        s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        self.check(msk_verify_step(self.h, io, s))
+
+    def close(self):
+        if self.h:
+            msk_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

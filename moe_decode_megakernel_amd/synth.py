@@ -263,3 +263,22 @@ def dev_normal_f32(t, seed, stream, std=1.0, stream_ptr=None):
 def dev_nvfp4(codes, scales, rows, cols, seed, stream, std, s_tensor, stream_ptr=None):
     _check(_dev().msk_synth_gpu_fill_nvfp4(codes.data_ptr(), scales.data_ptr(), rows, cols, seed, stream,
                                            std, float(s_tensor), stream_ptr))
+
+
+# ---------------------------------------------------------------------------
+# Upload of host arrays (torch tensors in device memory)
+# ---------------------------------------------------------------------------
+def to_device(arrays: dict, device="cuda") -> dict:
+    """numpy arrays -> torch tensors on `device` (same dtypes; uint16 as int16 bits)."""
+    import torch
+    out = {}
+    for name, a in arrays.items():
+        if a is None or not isinstance(a, np.ndarray):
+            out[name] = a
+            continue
+        if a.dtype == np.uint16:
+            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(a))
+        out[name] = t.to(device)
+    return out

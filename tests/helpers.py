@@ -1,0 +1,95 @@
+"""Shared helpers of the GPU parity tests: upload a seeded layer, run it
+through the C ABI with stage dumps, and run the oracle on the same inputs."""
+import sys
+
+import numpy as np
+
+from moe_decode_megakernel_amd import msk, synth
+from oracle import oracle as orc
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(got, ref):
+    """max |got - ref| / RMS(ref)."""
+    ref = np.asarray(ref, np.float64)
+    got = np.asarray(got, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    return float(np.max(np.abs(got - ref)) / rms) if rms > 0 else float(np.max(np.abs(got - ref)))
+
+
+def bf16_to_f64(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f16_to_f64(b):
+    return np.asarray(b, np.uint16).view(np.float16).astype(np.float64)
+
+
+class GpuLayerRun:
+    """One standalone layer on the GPU with every stage dumped."""
+
+    def __init__(self, w, lw, k, v, h, flags=0, dq_expert=-1, ctx=None):
+        import torch
+        self.torch = torch
+        dev = "cuda"
+        self.w = w
+        self.handle = msk.Handle(msk.make_config(w, n_layers=1, flags=flags))
+        self.t = synth.to_device(lw, dev)
+        self.t["k_cache"] = torch.from_numpy(k.view(np.int16)).to(dev)
+        self.t["v_cache"] = torch.from_numpy(v.view(np.int16)).to(dev)
+        self.handle.load_layer(0, self.t, int(lw["window"]))
+        NT = w.NT
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.h_in = torch.from_numpy(np.ascontiguousarray(h, np.float32)).to(dev)
+        self.h_out = torch.zeros((NT, w.H), **f32)
+        self.ids = torch.zeros((NT, w.k), dtype=torch.int32, device=dev)
+        self.gates = torch.zeros((NT, w.k), **f32)
+        self.dbg = {
+            "q": torch.zeros((NT, w.Dq), **f32), "k_new": torch.zeros((NT, w.Dkv), **f32),
+            "v_new": torch.zeros((NT, w.Dkv), **f32), "attn": torch.zeros((NT, w.Dq), **f32),
+            "h1": torch.zeros((NT, w.H), **f32), "n2": torch.zeros((NT, w.H), **f32),
+            "logits": torch.zeros((NT, w.E), **f32), "p": torch.zeros((NT, w.P), **f32),
+            "acc": torch.zeros((NT, w.P), **f32),
+            "dq_gate_up": torch.zeros((2 * w.I, w.P), dtype=torch.int16, device=dev),
+            "dq_down": torch.zeros((w.P, w.I), dtype=torch.int16, device=dev),
+        }
+        self.ctx = [w.ctx] * w.R if ctx is None else list(ctx)
+        self.dq_expert = dq_expert
+
+    def run(self, debug=True):
+        torch = self.torch
+        d = msk.make_debug(self.dbg, self.dq_expert) if debug else None
+        io = msk.make_io(self.w.R, self.w.T, self.ctx, self.h_in, self.h_out, self.ids, self.gates, d)
+        self.handle.verify_layer(0, io)
+        torch.cuda.synchronize()
+        out = {k: v.cpu().numpy() for k, v in self.dbg.items()}
+        out["h_out"] = self.h_out.cpu().numpy()
+        out["ids"] = self.ids.cpu().numpy()
+        out["gates"] = self.gates.cpu().numpy()
+        out["k_cache"] = self.t["k_cache"].cpu().numpy().view(np.uint16)
+        out["v_cache"] = self.t["v_cache"].cpu().numpy().view(np.uint16)
+        return out
+
+    def close(self):
+        self.handle.close()
+
+
+def oracle_layer(w, lw, k, v, h, use_norm=True, ctx=None):
+    ctx = [w.ctx] * w.R if ctx is None else list(ctx)
+    kk, vv = k.copy(), v.copy()
+    out, st = orc.layer_forward(w, lw, w.R, w.T, ctx, np.asarray(h, np.float64), kk, vv, w.cap,
+                                eps=w.eps, use_norm=use_norm)
+    st["h_out"] = out
+    st["k_cache"] = kk
+    st["v_cache"] = vv
+    return st
+
+
+def routing_margins(logits, k):
+    """Per token: gap between the k-th and (k+1)-th largest logit."""
+    s = -np.sort(-np.asarray(logits, np.float64), axis=1)
+    return s[:, k - 1] - s[:, k]
