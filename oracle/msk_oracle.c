@@ -25,8 +25,8 @@ int32_t orc_threads(void) {
 #endif
 }
 
-/* bf16 storage format of the dense layers and the KV cache ("some layers in
- * bf16"; the cache rows are bf16): value = the fp32 whose high half is b. */
+/* bf16, the storage format of the dense (non-expert) layers and of the KV
+ * cache (newruntime.com, What happened): value = the fp32 whose high half is b. */
 double orc_bf16_value(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
   float f;
@@ -59,7 +59,8 @@ uint16_t orc_bf16_rne(double x) {
   return (uint16_t)(sign | (uint16_t)((E + 127) << 7) | (uint16_t)((int)r - 128));
 }
 
-/* E2M1 element of NVFP4 ("expert weights are stored in 4-bit NVFP4"):
+/* E2M1 element of NVFP4, the 4-bit format of the expert weights
+ * (newruntime.com, What happened; OCP MX v1.0 for the element encoding):
  * sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
  * e > 0: 2^(e-1) * (1 + m/2); e = 0: m/2. */
 double orc_e2m1_value(uint8_t nibble) {
@@ -97,23 +98,33 @@ void orc_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, double s_ten
   }
 }
 
-/* The router's fp32 dot product in one fixed order: 64 partial sums, partial
- * j is an fma chain over the indices k = j (mod 64) in ascending order; then
- * pairwise halving (partial j += partial j+s for s = 32, 16, ..., 1).
- * The order is this build's reading (the pages fix none); it makes the fp32
- * top-k decision reproducible on both sides. */
+/* The router's fp32 dot product in one fixed order (this build's reading;
+ * the pages fix none): partial j is the fma chain over the 8 elements
+ * k = 8j .. 8j+7 in ascending order, starting from +0; the n/8 partials,
+ * padded with +0 to a power of two, are then added pairwise, adjacent pairs
+ * first (level by level). The order makes the fp32 top-k decision
+ * reproducible on both sides. n must be a multiple of 8. */
 float orc_dot_canon_f32(const float* x, const float* w, int32_t n) {
-  float part[64];
-  int32_t j, k, s;
-  for (j = 0; j < 64; ++j) part[j] = 0.0f;
-  for (k = 0; k < n; ++k) part[k & 63] = fmaf(x[k], w[k], part[k & 63]);
-  for (s = 32; s >= 1; s >>= 1)
-    for (j = 0; j < s; ++j) part[j] = part[j] + part[j + s];
-  return part[0];
+  int32_t np = n / 8, P = 1, j, i, len;
+  float* part;
+  float r;
+  while (P < np) P *= 2;
+  part = (float*)calloc((size_t)P, sizeof(float));
+  for (j = 0; j < np; ++j) {
+    float acc = 0.0f;
+    for (i = 0; i < 8; ++i) acc = fmaf(x[8 * j + i], w[8 * j + i], acc);
+    part[j] = acc;
+  }
+  for (len = P; len > 1; len /= 2)
+    for (j = 0; j < len / 2; ++j) part[j] = part[2 * j] + part[2 * j + 1];
+  r = part[0];
+  free(part);
+  return r;
 }
 
-/* Top-k of the router ("routes each token to 8 of 256 experts"): the k
- * largest logits, ordered by value descending, ties to the lower index. */
+/* Top-k of the router (8 of 256 experts per token; newruntime.com, What
+ * happened): the k largest logits, by value descending, ties to the lower
+ * index (the tie rule is this build's reading). */
 void orc_topk(const float* logits, int32_t n, int32_t k, int32_t* ids) {
   unsigned char* taken = (unsigned char*)calloc((size_t)n, 1);
   int32_t r, e;
@@ -189,8 +200,9 @@ static void linear_f64(const double* x, int32_t nt, const double* W, int32_t row
 }
 
 /*
- * Attention of one request's T verify tokens ("46 use sliding-window
- * attention over the previous 2,048 tokens and 16 use global attention").
+ * Attention of one request's T verify tokens. Of the 62 layers, 46 attend
+ * over a sliding window of the 2,048 most recent tokens and 16 over the whole
+ * context (newruntime.com, What happened; orcarouter.ai, model paragraph).
  * Token t sits at position ctx + t; query head h reads kv head h / (nq/nkv);
  * it sees keys j with j <= ctx + t (causal among the verify tokens) and, for a
  * window W > 0, j > ctx + t - W (W keys including itself). Scores are
@@ -238,18 +250,20 @@ void orc_attention(const double* q, const uint16_t* k_cache, const uint16_t* v_c
  * Steps, in order:
  *  1. n1 = RMSNorm(h) (gain g_attn); qkv = n1 Wqkv^T, rows Q | K | V.
  *  2. KV write: K and V of token t stored as bf16 at position ctx[r] + t of
- *     the request's cache ("attention through the next layer's QKV projection
- *     and KV write"); no other cache row changes.
+ *     the request's cache (a launch ends with the next layer's QKV
+ *     projection and KV write: newruntime.com, What happened); no other
+ *     cache row changes.
  *  3. Attention over the cache, including the rows just written.
  *  4. h1 = h + attn Wo^T.
  *  5. n2 = RMSNorm(h1) (gain g_moe).
  *  6. Router: fp32 logits = dot_canon(fl32(n2), Wr[e]) + b[e]; top-k; gates =
  *     softmax over the selected logits.
- *  7. Pooler ("shrinks each token vector before the experts"): p = n2 Wpool^T.
+ *  7. Pooler, which narrows the token vector ahead of the experts
+ *     (orcarouter.ai, model paragraph): p = n2 Wpool^T.
  *  8. Experts, SwiGLU on NVFP4 weights: gu = Wgu_e p (rows gate | up),
  *     a = silu(gate) * up, y = Wd_e a; acc = sum over the token's selected
  *     experts, in selection order, of gate weight * y.
- *  9. Unpooler ("restores it afterwards"): h2 = h1 + acc Wup^T.
+ *  9. Unpooler, which widens it back (same paragraph): h2 = h1 + acc Wup^T.
  * Caches are [R][nkv][cap][d] bf16. Returns 0, or -1 on bad arguments.
  */
 int32_t orc_layer_forward(const orc_layer* L, int32_t R, int32_t T, const int32_t* ctx,

@@ -82,21 +82,24 @@ def test_nvfp4_dequant_is_table_times_scales():
             assert Fraction(got[r, c]) == expect, (r, c)
 
 
-def test_router_order_hand_case():
-    rows = read_golden("router_order_case.txt")
-    n = int(rows[0][1])
-    w = np.zeros(n, np.float32)
-    expect = naive = None
-    for r in rows[1:]:
-        if r[0] == "k":
-            w[int(r[1])] = np.float32(float(r[2]))
+def test_router_order_hand_cases():
+    cases, cur = [], None
+    for r in read_golden("router_order_case.txt"):
+        if r[0] == "case":
+            cur = {"name": r[1], "w": np.zeros(int(r[2]), np.float32)}
+            cases.append(cur)
+        elif r[0] == "k":
+            cur["w"][int(r[1])] = np.float32(float(r[2]))
         elif r[0] == "expect":
-            expect = float(r[1])
-        elif r[0] == "naive":
-            naive = float(r[1])
-    x = np.ones(n, np.float32)
-    assert float(orc.dot_canon_f32(x, w)) == expect
-    assert float(np.float64(x.astype(np.float64) @ w.astype(np.float64))) == naive
+            cur["expect"] = float(r[1])
+        elif r[0] == "other":
+            cur["other"] = float(r[1])
+    assert [c["name"] for c in cases] == ["chain", "tree", "cancel"]
+    for c in cases:
+        x = np.ones(c["w"].size, np.float32)
+        got = float(orc.dot_canon_f32(x, c["w"]))
+        assert got == c["expect"], c["name"]
+        assert got != c["other"], c["name"]
 
 
 def test_router_dot_exact_on_small_integers():
@@ -113,8 +116,8 @@ def test_router_dot_within_fp32_error_bound():
         w = (rng.standard_normal(n) * 0.02).astype(np.float32)
         exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x, w))
         got = Fraction(float(orc.dot_canon_f32(x, w)))
-        # depth of the order: n/64 fma steps + 6 halving adds
-        depth = n // 64 + 6
+        # depth of the order: 8 fma steps + log2(n/8) pairwise adds
+        depth = 8 + int(np.log2(n // 8))
         u = 2.0 ** -24
         bound = depth * u / (1 - depth * u) * float(np.sum(np.abs(x.astype(np.float64) * w)))
         assert abs(float(got - exact)) <= bound
