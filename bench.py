@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-verify step on one MI355X.
+
+Default workload: the 62-layer verify step (16 tokens, 46 sliding-window
+layers of window 2048 and 16 global layers at 3, 7, ..., 59, 61, 16384-token
+caches, top-8 of 256 NVFP4 experts, Zipf-skewed routing, consecutive steps'
+inputs AR(1)-correlated). Weights (~63 GB) are filled on the device by the
+seeded generator; every timed step is one msk_verify_step call (62 resident
+layer launches) with inputs already in HBM.
+
+Prints one JSON line: step time (us), the HBM roofline of the layer kernel
+(algorithmic bytes / average launch time vs 8 TB/s), and the oracle's time on
+the host cores for a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "verify-step µs (16 tok, 62 layers) + achieved HBM TB/s vs ~8 TB/s peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="step62",
+                    choices=["step62", "swa_layer", "global_layer", "tiny_swa"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", default="0,3", help="layers of the step the oracle times")
+    ap.add_argument("--trace", action="store_true",
+                    help="after timing, run one step with the self-timing kernel and print the phase breakdown")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the verify step is not sharded across GPUs here).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from moe_decode_megakernel_amd import msk, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    w = synth.WORKLOADS[args.workload]
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    t0 = time.time()
+    handle = msk.Handle(msk.make_config(w))
+    layers = []
+    for l in range(w.n_layers):
+        t = synth.device_layer(w, l, dev, stream_ptr=stream.cuda_stream)
+        handle.load_layer(l, t, int(w.windows[l]))
+        layers.append(t)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: {w.n_layers} layers filled on the device in {time.time() - t0:.1f} s")
+
+    nsteps = args.warmup + args.steps
+    h_in = [torch.from_numpy(np.ascontiguousarray(synth.h_input(w, s), np.float32)).to(dev) for s in range(nsteps)]
+    h_out = torch.empty_like(h_in[0])
+    L = w.n_layers
+    ids = torch.zeros((nsteps, L, w.NT, w.k), dtype=torch.int32, device=dev)
+    gates = torch.zeros((nsteps, L, w.NT, w.k), dtype=torch.float32, device=dev)
+    ctx = [w.ctx] * w.R
+    ios = [msk.make_io(w.R, w.T, ctx, h_in[s], h_out, ids[s], gates[s]) for s in range(nsteps)]
+
+    def run(s):
+        if w.n_layers == 1:
+            handle.verify_layer(0, ios[s])
+        else:
+            handle.verify_step(ios[s])
+
+    for s in range(args.warmup):
+        run(s)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    per_step = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    per_step[0].record(stream)
+    for i in range(args.steps):
+        run(args.warmup + i)
+        per_step[i + 1].record(stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    step_ms = [per_step[i].elapsed_time(per_step[i + 1]) for i in range(args.steps)]
+    med_ms = float(np.median(step_ms))
+    mean_ms = total_ms / args.steps
+
+    # algorithmic bytes from the routing each timed step actually took
+    ids_h = ids.cpu().numpy()
+    step_bytes, nsel_all = [], []
+    for i in range(args.steps):
+        s = args.warmup + i
+        b = 0
+        for l in range(L):
+            n_sel = len(np.unique(ids_h[s, l]))
+            nsel_all.append(n_sel)
+            b += synth.algorithmic_bytes_per_layer(w, l, n_sel)
+        step_bytes.append(b)
+    mean_bytes = float(np.mean(step_bytes))
+    launches = L  # one resident layer kernel per layer boundary
+    avg_launch_us = mean_ms * 1e3 / launches
+    bytes_per_launch = mean_bytes / launches
+    achieved_gbs = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
+
+    # top-14 overlap between consecutive steps (routing correlation of the workload)
+    overlaps = []
+    for i in range(1, args.steps):
+        s = args.warmup + i
+        for l in range(L):
+            a = np.bincount(ids_h[s - 1, l].ravel(), minlength=w.E)
+            b = np.bincount(ids_h[s, l].ravel(), minlength=w.E)
+            ta = set(np.lexsort((np.arange(w.E), -a))[:14])
+            tb = set(np.lexsort((np.arange(w.E), -b))[:14])
+            overlaps.append(len(ta & tb) / 14.0)
+
+    result = {
+        "metric": METRIC if w.n_layers > 1 else f"verify-layer µs (16 tok, {w.name}) + achieved HBM TB/s",
+        "value": round(med_ms * 1e3, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "layers": w.n_layers, "tokens_per_request": w.T, "requests": w.R,
+            "ctx": w.ctx, "windows": "2048 (46 layers) / global (16 layers)" if w.n_layers == 62 else w.windows[0],
+            "hidden": w.H, "heads": f"{w.nq}q/{w.nkv}kv x {w.d}", "experts": f"top-{w.k} of {w.E}",
+            "pool": w.P, "expert_inter": w.I, "expert_format": "NVFP4 (E2M1 + E4M3/16 + fp32)",
+            "dense_format": "bf16", "router": "fp32",
+        },
+        "achieved_tbps": round(mean_bytes / (mean_ms * 1e-3) / 1e12, 3),
+        "hbm_frac": round(mean_bytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "us_per_layer": round(avg_launch_us, 2),
+        "distinct_experts_per_layer": round(float(np.mean(nsel_all)), 2),
+        "top14_overlap": round(float(np.mean(overlaps)), 3) if overlaps else None,
+        "step_ms_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
+        "roofline": {
+            "bound": "hbm", "kernel": "msk layer_kernel (one launch per layer boundary)",
+            "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+            "bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(avg_launch_us, 2),
+        },
+    }
+    log(f"[bench] median step {med_ms:.3f} ms, {result['achieved_tbps']} TB/s")
+    if args.trace:
+        result["trace"] = trace_breakdown(w, handle, h_in[-1], h_out, msk, torch, np, dev)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args)
+    print(json.dumps(result), flush=True)
+    handle.close()
+
+
+def trace_breakdown(w, handle, h_in_t, h_out_t, msk, torch, np, dev):
+    """One untimed step with the self-timing variant: per phase boundary, the
+    time (us since the launch's first workgroup started) at which the slowest
+    workgroup crossed it, averaged over the launches of each layer type."""
+    L = w.n_layers
+    trace = torch.zeros((L, msk.MAX_GRID, len(msk.TRACE_SLOTS)), dtype=torch.int64, device=dev)
+    io = msk.make_io(w.R, w.T, [w.ctx] * w.R, h_in_t, h_out_t, trace=trace)
+    if L == 1:
+        handle.verify_layer(0, io)
+    else:
+        handle.verify_step(io)
+    torch.cuda.synchronize()
+    tr = trace.cpu().numpy().astype(np.int64)
+    out = {}
+    groups = {"swa": [l for l in range(L) if w.windows[l] > 0 and 0 < l < L - 1],
+              "global": [l for l in range(L) if w.windows[l] <= 0 and 0 < l < L - 1]}
+    if L == 1:
+        groups = {"layer": [0]}
+    for name, ls in groups.items():
+        if not ls:
+            continue
+        acc, med = {}, {}
+        for l in ls:
+            t = tr[l]
+            started = t[:, 0] > 0
+            t0 = t[started, 0].min()
+            for si, sname in enumerate(msk.TRACE_SLOTS):
+                col = t[started, si]
+                if np.all(col == 0):
+                    continue
+                acc.setdefault(sname, []).append((col.max() - t0) * 0.01)
+                med.setdefault(sname, []).append((np.median(col[col > 0]) - t0) * 0.01)
+        out[name] = {k: round(float(np.mean(v)), 2) for k, v in acc.items()}
+        out[name + "_median_wg"] = {k: round(float(np.mean(v)), 2) for k, v in med.items()}
+        log(f"[trace] {name} (slowest wg): " + " ".join(f"{k}={v}" for k, v in out[name].items()))
+        log(f"[trace] {name} (median wg):  " + " ".join(f"{k}={v}" for k, v in out[name + '_median_wg'].items()))
+    return out
+
+
+def cpu_baseline(w, args):
+    """The oracle, as it stands, on the host cores, on a bounded sample of the
+    same workload: a few layers of the step, scaled to a whole step by layer
+    type (sliding-window vs global)."""
+    import numpy as np
+    from moe_decode_megakernel_amd import synth
+    from oracle import oracle as orc
+
+    sample_layers = [int(x) for x in args.cpu_layers.split(",")] if w.n_layers > 1 else [0]
+    times = {}
+    h = synth.h_input(w, 0).astype(np.float64)
+    for l in sample_layers:
+        lw = synth.layer_weights(w, l)
+        k, v = synth.kv_cache(w, l)
+        t0 = time.perf_counter()
+        orc.layer_forward(w, lw, w.R, w.T, [w.ctx] * w.R, h, k, v, w.cap, eps=w.eps, stages=False)
+        times[l] = time.perf_counter() - t0
+        del lw, k, v
+    swa = [times[l] for l in sample_layers if w.windows[l] > 0]
+    glb = [times[l] for l in sample_layers if w.windows[l] <= 0]
+    n_swa = sum(1 for x in w.windows if x > 0)
+    n_glb = len(w.windows) - n_swa
+    est = (np.mean(swa) if swa else np.mean(glb)) * n_swa + (np.mean(glb) if glb else np.mean(swa)) * n_glb
+    return {
+        "value": round(est * 1e6, 1), "unit": "us", "cores": orc.threads(), "kind": "oracle",
+        "sample": (f"layers {sample_layers} of {w.name} timed on the host "
+                   f"({', '.join(f'{l}: {times[l]:.2f} s' for l in sample_layers)}), scaled by layer type "
+                   f"to {n_swa} sliding-window + {n_glb} global layers; fp64 oracle, OpenMP over outputs"),
+    }
+
+
+if __name__ == "__main__":
+    main()

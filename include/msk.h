@@ -129,7 +129,20 @@ typedef struct {
   int32_t* expert_ids;    /* device, may be NULL: [L][R*T][k] (verify_layer: [R*T][k]) */
   float* gates;           /* device, may be NULL: same shape as expert_ids */
   const msk_debug* debug; /* HOST struct, may be NULL; honoured by msk_verify_layer */
+  uint64_t* trace;        /* device, may be NULL: self-timing variant of the kernel.
+                             [launch][256][MSK_TRACE_SLOTS] uint64 stamps of the GPU's
+                             100 MHz real-time counter, written by lane 0 of each
+                             workgroup at the phase boundaries below; slots a launch
+                             does not reach are left untouched. Exclusive with debug. */
 } msk_io;
+
+/* Trace slots, in execution order ("_BAR" = after the grid barrier that follows). */
+enum {
+  MSK_TR_START = 0, MSK_TR_QKV_OWN, MSK_TR_QKV_OWN_BAR, MSK_TR_ATTN, MSK_TR_ATTN_BAR,
+  MSK_TR_MERGE, MSK_TR_MERGE_BAR, MSK_TR_OPROJ, MSK_TR_OPROJ_BAR, MSK_TR_ROUTER_POOL,
+  MSK_TR_ROUTER_POOL_BAR, MSK_TR_GEMM1, MSK_TR_GEMM1_BAR, MSK_TR_GEMM2, MSK_TR_GEMM2_BAR,
+  MSK_TR_UNPOOL, MSK_TR_UNPOOL_BAR, MSK_TR_QKV_NEXT, MSK_TRACE_SLOTS
+};
 
 /* Bytes of device workspace a handle needs for this configuration; 0 if the
  * configuration is invalid. */

@@ -15,10 +15,10 @@
 
 namespace {
 
-constexpr int kMaxGrid = 256;  // workgroups per launch at most (one per compute unit)
+using msk::kMaxGrid;
 
 struct Layout {
-  size_t bar, sched, h1, ssq1, ssq2, hbuf0, hbuf1, qpart, apart, attn, logits, ppart, abuf, accpart, hist;
+  size_t bar, err, zeros, sched, h1, ssq1, ssq2, hbuf0, hbuf1, qpart, apart, attn, logits, ppart, abuf, accpart, hist;
   size_t total;
 };
 
@@ -36,27 +36,40 @@ struct TileSpec {
   bool splittable;
 };
 
-// Longest-processing-time assignment of units to G workgroups; splittable
-// tiles are cut into `slices` equal k ranges (slot = slice index).
+constexpr int kUnitMaxK = msk::kSubK * msk::kWaves;  // one 128-k sub-unit per wave
+
+// Longest-processing-time assignment of jobs to G workgroups. A splittable
+// tile becomes `slices` jobs of equal k ranges (partial slot = slice index);
+// an unsplit tile is one job. A job longer than one unit (kUnitMaxK) runs as
+// consecutive pieces on one workgroup, carrying the accumulator.
 SchedHost build_sched(const std::vector<TileSpec>& tiles, int slices, int G) {
-  std::vector<msk::Unit> all;
+  struct Job {
+    int tile, k0, klen, slot;
+  };
+  std::vector<Job> jobs;
   for (const TileSpec& t : tiles) {
     if (t.splittable && slices > 1) {
       int kl = t.klen / slices;
-      for (int s = 0; s < slices; ++s) all.push_back({t.tile, s * kl, kl, s});
+      for (int s = 0; s < slices; ++s) jobs.push_back({t.tile, s * kl, kl, s});
     } else {
-      all.push_back({t.tile, 0, t.klen, 0});
+      jobs.push_back({t.tile, 0, t.klen, 0});
     }
   }
-  std::stable_sort(all.begin(), all.end(), [](const msk::Unit& a, const msk::Unit& b) { return a.klen > b.klen; });
+  std::stable_sort(jobs.begin(), jobs.end(), [](const Job& a, const Job& b) { return a.klen > b.klen; });
   std::vector<std::vector<msk::Unit>> per(G);
   std::vector<int64_t> load(G, 0);
-  for (const msk::Unit& u : all) {
+  for (const Job& j : jobs) {
     int best = 0;
     for (int g = 1; g < G; ++g)
       if (load[g] < load[best]) best = g;
-    per[best].push_back(u);
-    load[best] += u.klen;
+    for (int k = 0; k < j.klen; k += kUnitMaxK) {
+      int kl = std::min(kUnitMaxK, j.klen - k);
+      int32_t slot = j.slot;
+      if (k == 0) slot |= msk::kUnitFirst;
+      if (k + kl == j.klen) slot |= msk::kUnitLast;
+      per[best].push_back({j.tile, j.k0 + k, kl, slot});
+    }
+    load[best] += j.klen;
   }
   SchedHost sh;
   sh.off.push_back(0);
@@ -74,7 +87,6 @@ SchedHost build_sched_best(const std::vector<TileSpec>& tiles, int K, int G, int
   int best_s = 1;
   for (int s : {1, 2, 4}) {
     if (K % (s * msk::kSubK) != 0) continue;
-    if (K / s > msk::kSubK * msk::kWaves * msk::kMaxSubPerWave) continue;
     SchedHost sh = build_sched(tiles, s, G);
     if (best.off.empty() || sh.max_load < best.max_load) {
       best = std::move(sh);
@@ -117,7 +129,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 std::string check_config(const msk_config* c) {
   if (!c) return "config is NULL";
   const int Dq = c->n_q_heads * c->head_dim;
-  if (c->hidden <= 0 || c->hidden % 128 != 0 || c->hidden > 4096) return "hidden must be a positive multiple of 128, <= 4096";
+  if (c->hidden < 128 || c->hidden > 4096 || (c->hidden & (c->hidden - 1)) != 0)
+    return "hidden must be a power of two in 128..4096";
   if (c->head_dim != 64 && c->head_dim != 128) return "head_dim must be 64 or 128";
   if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads != 0) return "n_q_heads must be a multiple of n_kv_heads";
   if (c->n_q_heads / c->n_kv_heads > msk::kWaves) return "at most 8 query heads per kv head";
@@ -148,9 +161,11 @@ Layout make_layout(const msk_config* c, int G) {
     o = align_up(o + bytes, 256);
     return at;
   };
-  L.bar = take(256);
+  L.bar = take(msk::kMaxGrid * 4);
+  L.err = take(256);
+  L.zeros = take(256);
   // schedule tables: units of 4 schedules + offsets (generous bound)
-  const size_t max_units = 4 * ((H / 16) * 4 + (Dq + 2 * c->n_kv_heads * c->head_dim) / 16 * 4 + (P / 16) * 4) + 64;
+  const size_t max_units = 4 * ((H / 16) * 4 + (Dq + 2 * c->n_kv_heads * c->head_dim) / 16 * 4 + (P / 16) * 4) * 2 + 64;
   L.sched = take(max_units * sizeof(msk::Unit) + 4 * (G + 1) * sizeof(int32_t));
   L.h1 = take(NT * H * 4);
   L.ssq1 = take((H / 16) * NT * 4);
@@ -158,7 +173,7 @@ Layout make_layout(const msk_config* c, int G) {
   L.hbuf0 = take(NT * H * 4);
   L.hbuf1 = take(NT * H * 4);
   L.qpart = take(4 * NT * Dq * 4);
-  L.apart = take((size_t)G * msk::kWaves * msk::kMaxTok * (c->head_dim + 2) * 4);
+  L.apart = take((size_t)G * msk::kWaves * msk::kMaxTok * (c->head_dim + 4) * 4);
   L.attn = take(NT * Dq * 2);
   L.logits = take(NT * E * 4);
   L.ppart = take(4 * NT * P * 4);
@@ -188,6 +203,7 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
   if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
     return fail(nullptr, MSK_E_HIP, "no HIP device");
   const int G = std::min(prop.multiProcessorCount, kMaxGrid);
+  if (cfg->n_experts > G) return fail(nullptr, MSK_E_SHAPE, "n_experts exceeds the workgroups of one launch (one router expert per workgroup)");
   Layout lay = make_layout(cfg, kMaxGrid);
   if (bytes < lay.total) return fail(nullptr, MSK_E_CAPACITY, "workspace smaller than msk_workspace_bytes");
 
@@ -240,6 +256,8 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
   // zero the barrier word, error word and routing histogram once
   std::vector<uint8_t> zeros(std::max<size_t>(256, (size_t)cfg->n_layers * cfg->n_experts * 4), 0);
   if (hipMemcpy(h->ws + lay.bar, zeros.data(), 256, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(h->ws + lay.err, zeros.data(), 256, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(h->ws + lay.zeros, zeros.data(), 256, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(h->ws + lay.hist, zeros.data(), (size_t)cfg->n_layers * cfg->n_experts * 4, hipMemcpyHostToDevice) != hipSuccess) {
     delete h;
     return fail(nullptr, MSK_E_HIP, "hipMemcpy of the workspace header failed");
@@ -306,6 +324,8 @@ msk_status check_io(msk_handle h, const msk_io* io) {
   }
   if (!io->h_in || !io->h_out) return fail(h, MSK_E_INVALID, "h_in and h_out are required");
   if (!aligned16(io->h_in) || !aligned16(io->h_out)) return fail(h, MSK_E_ALIGN, "h_in/h_out must be 16-byte aligned");
+  if (io->debug && io->trace) return fail(h, MSK_E_INVALID, "debug dumps and the trace are exclusive");
+  if (io->trace && !aligned16(io->trace)) return fail(h, MSK_E_ALIGN, "trace must be 16-byte aligned");
   if ((io->expert_ids && !aligned16(io->expert_ids)) || (io->gates && !aligned16(io->gates)))
     return fail(h, MSK_E_ALIGN, "expert_ids/gates must be 16-byte aligned");
   if (*h->err_host != 0) {
@@ -342,7 +362,7 @@ msk::Params base_params(msk_handle h, const msk_io* io) {
   p.p_slices = h->p_slices;
   uint8_t* ws = h->ws;
   p.bar = reinterpret_cast<uint32_t*>(ws + L.bar);
-  p.err = reinterpret_cast<int32_t*>(ws + L.bar + 64);
+  p.err = reinterpret_cast<int32_t*>(ws + L.err);
   p.h1 = reinterpret_cast<float*>(ws + L.h1);
   p.ssq1 = reinterpret_cast<float*>(ws + L.ssq1);
   p.ssq2 = reinterpret_cast<float*>(ws + L.ssq2);
@@ -354,6 +374,7 @@ msk::Params base_params(msk_handle h, const msk_io* io) {
   p.abuf = reinterpret_cast<uint16_t*>(ws + L.abuf);
   p.accpart = reinterpret_cast<float*>(ws + L.accpart);
   p.hist = reinterpret_cast<int32_t*>(ws + L.hist);
+  p.zeros = reinterpret_cast<const uint16_t*>(ws + L.zeros);
   p.s_qkv_own = h->s_qkv;
   p.s_qkv_next = h->s_qkv;
   p.s_oproj = h->s_oproj;
@@ -371,7 +392,7 @@ int barriers_of(uint32_t mode) {
 
 msk_status finish(msk_handle h, hipStream_t s) {
   const Layout& L = h->lay;
-  if (hipMemcpyAsync(h->err_host, h->ws + L.bar + 64, 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+  if (hipMemcpyAsync(h->err_host, h->ws + L.err, 4, hipMemcpyDeviceToHost, s) != hipSuccess)
     return fail(h, MSK_E_HIP, "hipMemcpyAsync of the error word failed");
   return MSK_OK;
 }
@@ -395,6 +416,8 @@ extern "C" msk_status msk_verify_layer(msk_handle h, int32_t layer, const msk_io
   p.h_out = io->h_out;
   p.out_ids = io->expert_ids;
   p.out_gates = io->gates;
+  p.trace = io->trace;
+  p.trace_launch = 0;
   bool debug = false;
   if (io->debug) {
     const msk_debug& d = *io->debug;
@@ -419,7 +442,7 @@ extern "C" msk_status msk_verify_step(msk_handle h, const msk_io* io, void* stre
   const int n = h->cfg.n_layers;
   const int NT = io->n_requests * io->n_tokens;
   float* hb[2] = {reinterpret_cast<float*>(h->ws + L.hbuf0), reinterpret_cast<float*>(h->ws + L.hbuf1)};
-  if (msk_launch_reset(reinterpret_cast<uint32_t*>(h->ws + L.bar), reinterpret_cast<int32_t*>(h->ws + L.bar + 64), s) != hipSuccess)
+  if (msk_launch_reset(reinterpret_cast<uint32_t*>(h->ws + L.bar), reinterpret_cast<int32_t*>(h->ws + L.err), s) != hipSuccess)
     return fail(h, MSK_E_HIP, "reset launch failed");
   uint32_t base = 0;
   for (int l = 0; l < n; ++l) {
@@ -433,6 +456,8 @@ extern "C" msk_status msk_verify_step(msk_handle h, const msk_io* io, void* stre
     p.h_out = (l == n - 1) ? io->h_out : hb[l & 1];
     p.out_ids = io->expert_ids ? io->expert_ids + (size_t)l * NT * h->cfg.top_k : nullptr;
     p.out_gates = io->gates ? io->gates + (size_t)l * NT * h->cfg.top_k : nullptr;
+    p.trace = io->trace;
+    p.trace_launch = l;
     hipError_t e = msk_launch_layer(p, h->grid, false, s);
     if (e != hipSuccess) return fail(h, MSK_E_HIP, std::string("layer launch failed: ") + hipGetErrorString(e));
     base += barriers_of(p.mode);

@@ -10,14 +10,15 @@ namespace msk {
 
 constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kThreads = kWaves * 64;     // threads per workgroup
+constexpr int kMaxGrid = 256;             // workgroups per launch at most (one per compute unit)
 constexpr int kMaxReq = 4;
 constexpr int kMaxTok = 16;               // tokens per launch handled as one 16-row MFMA tile
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 8;
 constexpr int kMaxHeadDim = 128;
 constexpr int kSubK = 128;                // dense k per wave sub-unit (4 MFMA steps of 32)
-constexpr int kMaxSubPerWave = 4;         // sub-units per wave per unit (unit k <= 4096)
 constexpr int kAttnChunk = 64;            // keys per attention chunk in LDS
+constexpr int kTraceSlots = 18;           // phase-boundary timestamps per workgroup per launch
 
 // Launch modes (bit set).
 enum : uint32_t {
@@ -25,9 +26,15 @@ enum : uint32_t {
   kModeQkvNext = 2u,  // last phase: QKV projection + KV write of the next layer
 };
 
-// Phase-work unit of a dense (bf16) projection: rows [tile*16, tile*16+16), k in [k0, k0+klen).
+// Phase-work unit of a dense (bf16) projection: rows [tile*16, tile*16+16),
+// k in [k0, k0+klen). A tile whose k range exceeds one unit is cut into
+// consecutive pieces on the same workgroup: the first piece starts the
+// accumulator, the last one reduces it and runs the epilogue.
+constexpr int32_t kUnitFirst = 1 << 30;
+constexpr int32_t kUnitLast = 1 << 29;
+constexpr int32_t kUnitSlotMask = 0xFFFF;
 struct Unit {
-  int32_t tile, k0, klen, slot;
+  int32_t tile, k0, klen, slot;  // slot: partial slot | kUnitFirst | kUnitLast
 };
 
 struct LayerW {
@@ -85,7 +92,7 @@ struct Params {
   const float* h_in;      // residual entering `layer`
   float* h_out;           // residual leaving `layer`
   // workspace
-  uint32_t* bar;          // grid barrier counter
+  uint32_t* bar;          // grid barrier flags [kMaxGrid] (sequence numbers)
   int32_t* err;           // device error word
   float* h1;              // [NT][H]
   float* ssq1;            // [H/16][NT] partial sums of squares of h1
@@ -98,11 +105,14 @@ struct Params {
   uint16_t* abuf;         // f16 [n_sel_max][NT][I]
   float* accpart;         // [parts][NT][P]
   int32_t* hist;          // [n_layers][E] selection counts
+  const uint16_t* zeros;  // 256 zero bytes (A operand of masked lanes)
   Sched s_qkv_own, s_qkv_next, s_oproj, s_pool, s_unpool;
   // outputs
   int32_t* out_ids;       // [NT][k] or NULL
   float* out_gates;
   Debug dbg;
+  uint64_t* trace;        // [launch][grid][kTraceSlots] or NULL (self-timing variant)
+  int32_t trace_launch;
 };
 
 }  // namespace msk

@@ -39,6 +39,7 @@ constexpr int kRedBytes = 2 * kWaves * 256 * 4;      // cross-wave partial tiles
 constexpr int kSmallBytes = 1024;
 
 struct Smem {
+  uint4 zero;  // 16 zero bytes: the A operand of lanes whose k range is out of bounds
   uint8_t x[kXBytes];
   float red[2][kWaves][256];
   float inv_rms[kMaxTok * kMaxReq];
@@ -77,49 +78,76 @@ __device__ __forceinline__ uint4 bf8_to_h8(uint4 v) {
   return make_uint4(bf2_to_h2(v.x), bf2_to_h2(v.y), bf2_to_h2(v.z), bf2_to_h2(v.w));
 }
 
+// Stores of data another workgroup reads later in the same launch are
+// write-through at agent scope (relaxed atomic stores, emitted with sc1), so
+// no dirty copy stays in one XCD's L2 and the grid barrier needs no L2
+// writeback or invalidate.
+__device__ __forceinline__ void st_wt(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_wt(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_wt(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// 16-byte write-through store (same cache policy as the scalar st_wt above).
+// The operand is taken as one whole vector: assembling it from scalar
+// bit-casts of its lanes has been compiled into a splat of lane 0.
+__device__ __forceinline__ void st_wt16(void* p, u32x4_t d) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(d) : "memory");
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // ---------------------------------------------------------------------------
-// Grid barrier: every wave publishes its stores (release fence), the
-// workgroup meets, one thread adds to the counter; waiting is a bounded spin
-// on the counter followed by an acquire fence in every wave.
+// Grid barrier. All data exchanged between workgroups inside a launch is
+// written with write-through stores (st_wt) and read with ordinary loads, and
+// no workgroup reads such a buffer before the phase that writes it (caches
+// start clean at the launch boundary). Arriving: every wave waits for its
+// stores to complete (s_waitcnt vmcnt(0)), the workgroup meets, and one
+// thread publishes the barrier's sequence number in the workgroup's own flag
+// word (write-through). Waiting: thread i polls workgroup i's flag until it
+// reaches the sequence number (bounded spin), then the workgroup meets again.
+// Flags are packed 16 per 64-byte line. No atomics, no L2 writeback or
+// invalidate. Sequence numbers grow through a call (reset at its start).
 // ---------------------------------------------------------------------------
 struct Barrier {
-  uint32_t* ctr;
+  uint32_t* flags;  // [grid] sequence numbers
   int32_t* err;
-  uint32_t target;  // counter value that completes the next barrier
-  uint32_t step;    // increment of target per barrier (= grid size)
+  uint32_t seq;     // sequence number of the next barrier
 };
 
-__device__ void bar_arrive(Barrier& b) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+__device__ __forceinline__ void bar_arrive(Barrier& b) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(b.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&b.flags[blockIdx.x], b.seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Returns false if the launch must stop (timeout or an error raised elsewhere).
-__device__ bool bar_wait(Barrier& b, Smem& sm) {
-  if (threadIdx.x == 0) {
-    int32_t ok = 1;
-    uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (true) {
-      uint32_t v = __hip_atomic_load(b.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (v >= b.target) break;
-      if (__hip_atomic_load(b.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { ok = 0; break; }
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
-        __hip_atomic_store(b.err, kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = 0;
-        break;
+__device__ __forceinline__ bool bar_wait(Barrier& b, Smem& sm) {
+  if (threadIdx.x == 0) sm.flag = 1;
+  __syncthreads();
+  if (threadIdx.x < gridDim.x) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    uint32_t polls = 0;
+    while (__hip_atomic_load(&b.flags[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < b.seq) {
+      if ((++polls & 63u) == 0) {
+        if (__hip_atomic_load(b.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { sm.flag = 0; break; }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+          __hip_atomic_store(b.err, kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          sm.flag = 0;
+          break;
+        }
       }
-      __builtin_amdgcn_s_sleep(1);
     }
-    sm.flag = ok;
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  bool ok = sm.flag != 0;
-  b.target += b.step;
+  const bool ok = sm.flag != 0;
+  b.seq += 1;
   __syncthreads();
   return ok;
 }
@@ -137,7 +165,7 @@ __device__ __forceinline__ uint4 lds_x_read(const Smem& sm, int K, int row, int 
 // inv_rms[t] = 1/sqrt(mean(h_t^2) + eps), from per-tile partial sums (ssq
 // [ntiles][NT], summed in tile order) or, when ssq is NULL, from h directly
 // (lane j sums k = j mod 64 ascending, then pairwise halving).
-__device__ void compute_inv_rms(const Params& p, const float* h, const float* ssq, Smem& sm) {
+__device__ __forceinline__ void compute_inv_rms(const Params& p, const float* h, const float* ssq, Smem& sm) {
   const int NT = p.NT, H = p.H;
   if (!p.use_norm) {
     if (threadIdx.x < kMaxTok) sm.inv_rms[threadIdx.x] = 1.0f;
@@ -145,11 +173,19 @@ __device__ void compute_inv_rms(const Params& p, const float* h, const float* ss
     return;
   }
   if (ssq) {
-    if (threadIdx.x < NT) {
-      float s = 0.0f;
-      const int nt = H / 16;
-      for (int i = 0; i < nt; ++i) s += ssq[i * NT + threadIdx.x];
-      sm.inv_rms[threadIdx.x] = rsqrtf(s / (float)H + p.eps);
+    // lane j sums tile partials j, j+64, ... in order, then pairwise halving
+    const int lane = lane_id();
+    const int nt = H / 16;
+    for (int t = wave_id(); t < NT; t += kWaves) {
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = lane + q * 64;
+        if (i < nt) v[q] = ssq[i * NT + t];
+      }
+      float s = ((v[0] + v[1]) + v[2]) + v[3];
+      for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+      if (lane == 0) sm.inv_rms[t] = rsqrtf(s / (float)H + p.eps);
     }
   } else {
     const int lane = lane_id();
@@ -166,8 +202,11 @@ __device__ void compute_inv_rms(const Params& p, const float* h, const float* ss
   __syncthreads();
 }
 
-// X = fp16(h * inv_rms * g) (or fp16(h) without the norm), rounded to nearest even.
-__device__ void fill_x_norm(const Params& p, const float* h, const uint16_t* g, Smem& sm) {
+// X = fp16(h * inv_rms * g), or fp16(h * g) when the caller applies inv_rms to
+// the projection's output instead (with_inv = false), or fp16(h) without the
+// norm; rounded to nearest even.
+__device__ __forceinline__ void fill_x_norm(const Params& p, const float* h, const uint16_t* g, Smem& sm,
+                                            bool with_inv = true) {
   const int K = p.H, NT = p.NT, K8 = K / 8;
   for (int i = threadIdx.x; i < kMaxTok * K8; i += kThreads) {
     int t = i / K8, k = (i % K8) * 8;
@@ -176,7 +215,7 @@ __device__ void fill_x_norm(const Params& p, const float* h, const uint16_t* g, 
       const float4* hp = reinterpret_cast<const float4*>(h + (size_t)t * K + k);
       float4 a = hp[0], b = hp[1];
       float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      float inv = sm.inv_rms[t];
+      const float inv = with_inv ? sm.inv_rms[t] : 1.0f;
       if (p.use_norm) {
         uint4 gg = *reinterpret_cast<const uint4*>(g + k);
         uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
@@ -196,8 +235,43 @@ __device__ void fill_x_norm(const Params& p, const float* h, const uint16_t* g, 
   __syncthreads();
 }
 
+// QKV input of the next layer: X = fp16(h * g) (the RMSNorm scale is applied
+// to the projection's output), and inv_rms from the tile partial sums; the
+// partial sums are requested before the fill so both round trips overlap.
+__device__ __forceinline__ void fill_x_qkv(const Params& p, const float* h, const uint16_t* g, const float* ssq,
+                                           Smem& sm) {
+  const int lane = lane_id(), w = wave_id(), NT = p.NT, H = p.H;
+  const int nt = H / 16;
+  float v[2][4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int t = min(w + r * kWaves, NT - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = min(lane + q * 64, nt - 1);
+      v[r][q] = ssq[i * NT + t];
+    }
+  }
+  fill_x_norm(p, h, g, sm, false);
+  if (p.use_norm) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int t = w + r * kWaves;
+      float s = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (lane + q * 64 < nt) s += v[r][q];
+      for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+      if (lane == 0 && t < NT) sm.inv_rms[t] = rsqrtf(s / (float)H + p.eps);
+    }
+  } else if (threadIdx.x < kMaxTok) {
+    sm.inv_rms[threadIdx.x] = 1.0f;
+  }
+  __syncthreads();
+}
+
 // X = copy of a 16-bit activation matrix src [NT][K] (already fp16).
-__device__ void fill_x_copy(const uint16_t* src, int K, int NT, Smem& sm) {
+__device__ __forceinline__ void fill_x_copy(const uint16_t* src, int K, int NT, Smem& sm) {
   const int K8 = K / 8;
   for (int i = threadIdx.x; i < kMaxTok * K8; i += kThreads) {
     int t = i / K8, k = (i % K8) * 8;
@@ -209,7 +283,7 @@ __device__ void fill_x_copy(const uint16_t* src, int K, int NT, Smem& sm) {
 }
 
 // X = sum over n partial slots of fp32 [n][NT][K], rounded to fp16.
-__device__ void fill_x_sum(const float* parts, int n, int K, int NT, Smem& sm) {
+__device__ __forceinline__ void fill_x_sum(const float* parts, int n, int K, int NT, Smem& sm) {
   const int K8 = K / 8;
   for (int i = threadIdx.x; i < kMaxTok * K8; i += kThreads) {
     int t = i / K8, k = (i % K8) * 8;
@@ -231,48 +305,50 @@ __device__ void fill_x_sum(const float* parts, int n, int K, int NT, Smem& sm) {
 }
 
 // ---------------------------------------------------------------------------
-// Dense projection (bf16 weights): Y[t][n] = sum_k X[t][k] W[n][k] over the units of
-// this workgroup. Each unit (16 rows x klen) is split over the 8 waves in
-// sub-units of 128 k (sub-unit j goes to wave j % 8); lane (r, g) loads 16 B
-// of row r at k = sub*128 + s*32 + g*8 (s = 0..3), converts it to fp16 and
-// feeds one MFMA per load.
-// The 8 per-wave 16x16 partials are summed in LDS in wave order.
-// Two units are kept in flight: the next unit's loads are issued before the
-// current one is reduced.
+// Dense projection (bf16 weights): Y[t][n] = sum_k X[t][k] W[n][k] over the
+// units of this workgroup. A unit is 16 weight rows x klen (<= 1024) k; wave
+// w owns the 128-k sub-unit w: lane (r, g) loads 16 B of row r at
+// k = k0 + w*128 + s*32 + g*8 (s = 0..3), converts it to fp16 and feeds one
+// MFMA per load. The 8 per-wave 16x16 partials are summed in LDS in wave
+// order. A wave whose sub-unit lies beyond klen loads a clamped in-range
+// address and reads the zero A operand, so every wave issues the same loads
+// for every unit: the compiler can count them, and kRing units of loads stay
+// in flight across unit boundaries.
 // ---------------------------------------------------------------------------
-struct DenseBuf {
-  uint4 b[kMaxSubPerWave][4];
+constexpr int kRing = 4;
+
+struct DenseSlot {
+  uint4 b[4];
+  float res;  // residual of this thread's (token, row) output (epilogues that add one)
 };
 
-__device__ __forceinline__ void dense_load(const uint16_t* W, int ldw, const Unit& u, DenseBuf& buf) {
+template <bool RES>
+__device__ __forceinline__ void dense_issue(const Unit& u, const uint16_t* W, int ldw, const float* res, int H,
+                                            int NT, DenseSlot& sl) {
   const int lane = lane_id(), r = lane & 15, g = lane >> 4, w = wave_id();
-  const int nsub = u.klen / kSubK;
-  const uint16_t* row = W + (size_t)(u.tile * 16 + r) * ldw + u.k0 + g * 8;
+  const bool valid = w * kSubK < u.klen;
+  const int k = u.k0 + (valid ? w * kSubK : 0) + g * 8;
+  const uint16_t* row = W + (size_t)(u.tile * 16 + r) * ldw + k;
 #pragma unroll
-  for (int c = 0; c < kMaxSubPerWave; ++c) {
-    int j = w + c * kWaves;
-    if (j < nsub) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        buf.b[c][s] = *reinterpret_cast<const uint4*>(row + j * kSubK + s * 32);
-    }
+  for (int q = 0; q < 4; ++q) sl.b[q] = *reinterpret_cast<const uint4*>(row + q * 32);
+  if constexpr (RES) {
+    const int tid = threadIdx.x & 255;
+    const int tok = min(tid >> 4, NT - 1);
+    sl.res = res[(size_t)tok * H + u.tile * 16 + (tid & 15)];
   }
 }
 
-__device__ __forceinline__ f32x4_t dense_compute(const Smem& sm, int K, const Unit& u, const DenseBuf& buf) {
+__device__ __forceinline__ f32x4_t dense_compute(const Smem& sm, int K, const Unit& u, const DenseSlot& sl,
+                                                 f32x4_t acc) {
   const int lane = lane_id(), r = lane & 15, g = lane >> 4, w = wave_id();
-  const int nsub = u.klen / kSubK;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const bool valid = w * kSubK < u.klen;
+  const uint8_t* abase = valid ? sm.x + r * x_stride(K) + (u.k0 + w * kSubK + g * 8) * 2
+                               : reinterpret_cast<const uint8_t*>(&sm.zero);
+  const int astep = valid ? 64 : 0;
 #pragma unroll
-  for (int c = 0; c < kMaxSubPerWave; ++c) {
-    int j = w + c * kWaves;
-    if (j < nsub) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        uint4 a = lds_x_read(sm, K, r, u.k0 + j * kSubK + s * 32 + g * 8);
-        acc = mfma_f16(a, bf8_to_h8(buf.b[c][s]), acc);
-      }
-    }
+  for (int q = 0; q < 4; ++q) {
+    const uint4 a = *reinterpret_cast<const uint4*>(abase + q * astep);
+    acc = mfma_f16(a, bf8_to_h8(sl.b[q]), acc);
   }
   return acc;
 }
@@ -303,7 +379,8 @@ __device__ __forceinline__ float sum16(float v) {
 enum class Epi { Qkv, OProj, Pool, Unpool };
 
 struct EpiArgs {
-  const LayerW* lw;  // layer of a QKV epilogue
+  uint16_t* k_cache;  // QKV epilogue: caches of the projected layer
+  uint16_t* v_cache;
   const float* res;  // residual input (OProj: h, Unpool: h1)
   float* out;        // OProj: h1, Unpool: h_out, Pool: ppart, Qkv: qpart
   float* ssq;        // partial sums of squares (OProj, Unpool)
@@ -313,7 +390,7 @@ struct EpiArgs {
 
 template <Epi E>
 __device__ __forceinline__ void dense_epilogue(const Params& p, const EpiArgs& ea, const Unit& u,
-                                               const Smem& sm, int rb) {
+                                               const Smem& sm, int rb, float res) {
   const int tid = threadIdx.x;
   if (tid >= 256) return;
   const int tok = tid >> 4, row = tid & 15;
@@ -323,8 +400,9 @@ __device__ __forceinline__ void dense_epilogue(const Params& p, const EpiArgs& e
   if constexpr (E == Epi::Qkv) {
     const int Dq = p.nq * p.d, Dkv = p.nkv * p.d;
     if (tok < NT) {
+      v *= sm.inv_rms[tok];
       if (n < Dq) {
-        ea.out[((size_t)u.slot * NT + tok) * Dq + n] = v;
+        st_wt(&ea.out[((size_t)(u.slot & kUnitSlotMask) * NT + tok) * Dq + n], v);
       } else {
         int c = n - Dq;
         bool is_v = c >= Dkv;
@@ -333,63 +411,66 @@ __device__ __forceinline__ void dense_epilogue(const Params& p, const EpiArgs& e
         int r = tok / p.T, t = tok % p.T;
         size_t dst = (((size_t)r * p.nkv + g) * p.cap + p.ctx[r] + t) * p.d + cc;
         if (is_v) {
-          ea.lw->v_cache[dst] = f2bf(v);
+          st_wt(&ea.v_cache[dst], f2bf(v));
           if (ea.dbg_v) ea.dbg_v[(size_t)tok * Dkv + c] = v;
         } else {
-          ea.lw->k_cache[dst] = f2bf(v);
+          st_wt(&ea.k_cache[dst], f2bf(v));
           if (ea.dbg_k) ea.dbg_k[(size_t)tok * Dkv + c] = v;
         }
       }
     }
   } else if constexpr (E == Epi::Pool) {
-    if (tok < NT) ea.out[((size_t)u.slot * NT + tok) * p.P + n] = v;
+    if (tok < NT) st_wt(&ea.out[((size_t)(u.slot & kUnitSlotMask) * NT + tok) * p.P + n], v);
   } else {
     // OProj / Unpool: residual add, then partial sum of squares over the tile's 16 rows.
     float h = 0.0f;
     if (tok < NT) {
-      h = ea.res[(size_t)tok * p.H + n] + v;
-      ea.out[(size_t)tok * p.H + n] = h;
+      h = res + v;
+      st_wt(&ea.out[(size_t)tok * p.H + n], h);
     }
     float s = sum16(h * h);
-    if (row == 0 && tok < NT) ea.ssq[u.tile * NT + tok] = s;
+    if (row == 0 && tok < NT) st_wt(&ea.ssq[u.tile * NT + tok], s);
   }
 }
 
-// Runs this workgroup's dense units; the first unit's weights may already be
-// in `first` (loaded before a barrier).
+// Runs this workgroup's dense units; the first kRing units' weights are
+// already in flight in the ring (requested by dense_prefetch before the
+// preceding barrier wait).
 template <Epi E>
-__device__ void dense_phase(const Params& p, const Sched& sc, const uint16_t* W, int ldw, int K,
-                            const EpiArgs& ea, Smem& sm, DenseBuf& first, bool have_first) {
+__device__ __forceinline__ void dense_phase(const Params& p, const Sched& sc, const uint16_t* W, int ldw, int K,
+                                            const EpiArgs& ea, Smem& sm, DenseSlot (&ring)[kRing]) {
+  constexpr bool RES = E == Epi::OProj || E == Epi::Unpool;
   const int b0 = sc.off[blockIdx.x], b1 = sc.off[blockIdx.x + 1];
   if (b0 >= b1) return;
-  DenseBuf bufA, bufB;
-  bufA = first;
-  if (!have_first) dense_load(W, ldw, sc.units[b0], bufA);
   int rb = 0;
-  for (int i = b0; i < b1; i += 2) {
-    Unit u0 = sc.units[i];
-    bool has1 = i + 1 < b1;
-    Unit u1 = has1 ? sc.units[i + 1] : u0;
-    if (has1) dense_load(W, ldw, u1, bufB);
-    f32x4_t acc = dense_compute(sm, K, u0, bufA);
-    red_store(sm, rb, acc);
-    __syncthreads();
-    dense_epilogue<E>(p, ea, u0, sm, rb);
-    rb ^= 1;
-    if (!has1) break;
-    if (i + 2 < b1) dense_load(W, ldw, sc.units[i + 2], bufA);
-    acc = dense_compute(sm, K, u1, bufB);
-    red_store(sm, rb, acc);
-    __syncthreads();
-    dense_epilogue<E>(p, ea, u1, sm, rb);
-    rb ^= 1;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int base = b0; base < b1; base += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      const int ui = base + i;
+      const Unit u = sc.units[min(ui, b1 - 1)];
+      if (u.slot & kUnitFirst) acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc = dense_compute(sm, K, u, ring[i], acc);
+      if (ui < b1 && (u.slot & kUnitLast)) {
+        red_store(sm, rb, acc);
+        __syncthreads();
+        dense_epilogue<E>(p, ea, u, sm, rb, ring[i].res);
+        rb ^= 1;
+      }
+      dense_issue<RES>(sc.units[min(ui + kRing, b1 - 1)], W, ldw, ea.res, p.H, p.NT, ring[i]);
+    }
   }
   __syncthreads();
 }
 
-__device__ __forceinline__ void dense_prefetch(const Sched& sc, const uint16_t* W, int ldw, DenseBuf& buf) {
+template <Epi E>
+__device__ __forceinline__ void dense_prefetch(const Params& p, const Sched& sc, const uint16_t* W, int ldw,
+                                               const float* res, DenseSlot (&ring)[kRing]) {
+  constexpr bool RES = E == Epi::OProj || E == Epi::Unpool;
   const int b0 = sc.off[blockIdx.x], b1 = sc.off[blockIdx.x + 1];
-  if (b0 < b1) dense_load(W, ldw, sc.units[b0], buf);
+  if (b0 >= b1) return;
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) dense_issue<RES>(sc.units[min(b0 + i, b1 - 1)], W, ldw, res, p.H, p.NT, ring[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -410,14 +491,14 @@ __device__ __forceinline__ void attn_range(const Params& p, const LayerW& lw, in
 }
 
 __device__ __forceinline__ int attn_splits(const Params& p, int nkeys, int grid) {
-  int cap_s = grid / (p.R * p.nkv);
+  int cap_s = min(64, grid / (p.R * p.nkv));  // the merge keeps one split per lane
   if (cap_s < 1) cap_s = 1;
   int s = (nkeys + 255) / 256;
   return s < 1 ? 1 : (s > cap_s ? cap_s : s);
 }
 
 // Item of a flat index; returns false if idx is past the last item.
-__device__ bool attn_item(const Params& p, const LayerW& lw, int idx, int grid, AttnItem& it) {
+__device__ __forceinline__ bool attn_item(const Params& p, const LayerW& lw, int idx, int grid, AttnItem& it) {
   for (int r = 0; r < p.R; ++r) {
     int lo, hi;
     attn_range(p, lw, r, lo, hi);
@@ -440,7 +521,7 @@ __device__ bool attn_item(const Params& p, const LayerW& lw, int idx, int grid, 
 }
 
 // Index of the first item of (r, g) in the flat order.
-__device__ int attn_item_base(const Params& p, const LayerW& lw, int r, int g, int grid, int& S) {
+__device__ __forceinline__ int attn_item_base(const Params& p, const LayerW& lw, int r, int g, int grid, int& S) {
   int base = 0;
   for (int rr = 0; rr < p.R; ++rr) {
     int lo, hi;
@@ -456,13 +537,14 @@ __device__ int attn_item_base(const Params& p, const LayerW& lw, int r, int g, i
   return base;
 }
 
-// Partial record of (item, wave, token): o[d], then m, l.
+// Partial record of (item, wave, token): o[d], then m, l (stride d + 4 floats,
+// so every record starts 16-byte aligned).
 __device__ __forceinline__ float* apart_at(const Params& p, int item, int w, int t) {
-  return p.apart + (((size_t)item * kWaves + w) * kMaxTok + t) * (p.d + 2);
+  return p.apart + (((size_t)item * kWaves + w) * kMaxTok + t) * (p.d + 4);
 }
 
 template <int D>
-__device__ void attention_phase(const Params& p, const LayerW& lw, Smem& sm) {
+__device__ __forceinline__ void attention_phase(const Params& p, const LayerW& lw, Smem& sm) {
   AttnItem it;
   if (!attn_item(p, lw, blockIdx.x, gridDim.x, it)) return;
   const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4, w = wave_id();
@@ -474,9 +556,10 @@ __device__ void attention_phase(const Params& p, const LayerW& lw, Smem& sm) {
   const int window = lw.window;
   constexpr int KS = D / 32;     // MFMA steps over the head dim
   constexpr int DT = D / 16;     // d tiles of the PV product
-  constexpr int RS = D + 8;      // LDS row stride (elements)
+  constexpr int RS = D + 8;               // K tile row stride (elements): Ks[key][d]
+  constexpr int VS = kAttnChunk + 4;      // V^T tile row stride (elements): Vt[d][key]
   uint16_t* Ks = reinterpret_cast<uint16_t*>(sm.x);
-  uint16_t* Vs = Ks + kAttnChunk * RS;
+  uint16_t* Vt = Ks + kAttnChunk * RS;
 
   // Q^T operand: col = token r_, 8 consecutive dims per lane group, summed over slices.
   uint4 qb[KS];
@@ -514,21 +597,21 @@ __device__ void attention_phase(const Params& p, const LayerW& lw, Smem& sm) {
   constexpr int PER = (CH16 + kThreads - 1) / kThreads;
   const int nchunks = (it.k_end - it.k_begin + kAttnChunk - 1) / kAttnChunk;
 
+  // K pieces: consecutive threads walk a key's dims (coalesced rows);
+  // V pieces: consecutive threads walk keys at fixed dims, so the transposed
+  // LDS writes of a wave land on consecutive addresses.
   uint4 kreg[PER], vreg[PER];
   auto load_chunk = [&](int c) {
     int kb = it.k_begin + c * kAttnChunk;
+    static_assert(CH16 % kThreads == 0, "a chunk is a whole number of 16-byte pieces per thread");
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       int i = threadIdx.x + j * kThreads;
-      kreg[j] = make_uint4(0, 0, 0, 0);
-      vreg[j] = make_uint4(0, 0, 0, 0);
-      if (i < CH16) {
-        int key = i / (D / 8), c8 = (i % (D / 8)) * 8;
-        if (kb + key < it.k_end) {
-          kreg[j] = *reinterpret_cast<const uint4*>(kc + (size_t)(kb + key) * D + c8);
-          vreg[j] = *reinterpret_cast<const uint4*>(vc + (size_t)(kb + key) * D + c8);
-        }
-      }
+      // keys past the item's end read its last row (finite values, masked later)
+      const int key = i / (D / 8), c8 = (i % (D / 8)) * 8;
+      kreg[j] = *reinterpret_cast<const uint4*>(kc + (size_t)min(kb + key, it.k_end - 1) * D + c8);
+      const int vkey = i % kAttnChunk, vc8 = (i / kAttnChunk) * 8;
+      vreg[j] = *reinterpret_cast<const uint4*>(vc + (size_t)min(kb + vkey, it.k_end - 1) * D + vc8);
     }
   };
   if (nchunks > 0) load_chunk(0);
@@ -537,10 +620,17 @@ __device__ void attention_phase(const Params& p, const LayerW& lw, Smem& sm) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       int i = threadIdx.x + j * kThreads;
-      if (i < CH16) {
+      {
         int key = i / (D / 8), c8 = (i % (D / 8)) * 8;
         *reinterpret_cast<uint4*>(Ks + key * RS + c8) = bf8_to_h8(kreg[j]);
-        *reinterpret_cast<uint4*>(Vs + key * RS + c8) = bf8_to_h8(vreg[j]);
+        int vkey = i % kAttnChunk, vc8 = (i / kAttnChunk) * 8;
+        const uint4 vh = bf8_to_h8(vreg[j]);
+        const uint32_t vw[4] = {vh.x, vh.y, vh.z, vh.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          Vt[(vc8 + 2 * q) * VS + vkey] = (uint16_t)(vw[q] & 0xFFFFu);
+          Vt[(vc8 + 2 * q + 1) * VS + vkey] = (uint16_t)(vw[q] >> 16);
+        }
       }
     }
     if (c + 1 < nchunks) load_chunk(c + 1);
@@ -601,12 +691,10 @@ __device__ void attention_phase(const Params& p, const LayerW& lw, Smem& sm) {
       const int k0 = u * 32 + 4 * g_;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int col = dt * 16 + r_;
-        uint16_t v0 = Vs[(k0 + 0) * RS + col], v1 = Vs[(k0 + 1) * RS + col];
-        uint16_t v2 = Vs[(k0 + 2) * RS + col], v3 = Vs[(k0 + 3) * RS + col];
-        uint16_t v4 = Vs[(k0 + 16) * RS + col], v5 = Vs[(k0 + 17) * RS + col];
-        uint16_t v6 = Vs[(k0 + 18) * RS + col], v7 = Vs[(k0 + 19) * RS + col];
-        uint4 av = make_uint4(pack2(v0, v1), pack2(v2, v3), pack2(v4, v5), pack2(v6, v7));
+        const uint16_t* vrow = Vt + (dt * 16 + r_) * VS;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + k0);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + k0 + 16);
+        uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
         o[dt] = mfma_f16(av, bp, o[dt]);
       }
     }
@@ -615,72 +703,161 @@ __device__ void attention_phase(const Params& p, const LayerW& lw, Smem& sm) {
     float* rec = apart_at(p, blockIdx.x, w, r_);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rec[dt * 16 + 4 * g_ + i] = o[dt][i];
+      st_wt16(rec + dt * 16 + 4 * g_, __builtin_bit_cast(u32x4_t, o[dt]));
     if (g_ == 0) {
-      rec[D] = m_run;
-      rec[D + 1] = l_run;
+      const f32x4_t ml = {m_run, l_run, 0.0f, 0.0f};
+      st_wt16(rec + D, __builtin_bit_cast(u32x4_t, ml));
     }
   }
 }
 
-// Merge of the split partials: one thread per (token, q head, dim).
-__device__ void merge_phase(const Params& p, const LayerW& lw, bool debug) {
+// Merge of the split partials (log-sum-exp in base 2): one wave per
+// (token, q head) row; lane s < S holds split s's (m, l), lanes split the dims.
+template <bool debug>
+__device__ __forceinline__ void merge_phase(const Params& p, const LayerW& lw) {
   const int D = p.d, Dq = p.nq * D, group = p.nq / p.nkv;
-  const int total = p.NT * p.nq * D;
-  for (int i = blockIdx.x * kThreads + threadIdx.x; i < total; i += gridDim.x * kThreads) {
-    const int c = i % D, h = (i / D) % p.nq, tok = i / (D * p.nq);
+  const int lane = lane_id();
+  const int rows = p.NT * p.nq;
+  const int nw = gridDim.x * kWaves;
+  for (int row = blockIdx.x * kWaves + wave_id(); row < rows; row += nw) {
+    const int h = row % p.nq, tok = row / p.nq;
     const int r = tok / p.T, t = tok % p.T;
     const int g = h / group, w = h % group;
     int S;
     const int base = attn_item_base(p, lw, r, g, gridDim.x, S);
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, apart_at(p, base + s, w, t)[D]);
-    float L = 0.0f, O = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float* rec = apart_at(p, base + s, w, t);
-      float m = rec[D];
-      float f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-      L += rec[D + 1] * f;
-      O += rec[c] * f;
+    float m = -INFINITY, l = 0.0f;
+    if (lane < S) {
+      const float* rec = apart_at(p, base + lane, w, t);
+      m = rec[D];
+      l = rec[D + 1];
     }
-    float out = O / L;
-    p.attn[(size_t)tok * Dq + h * D + c] = f2h(out);
-    if (debug && p.dbg.attn) p.dbg.attn[(size_t)tok * Dq + h * D + c] = out;
+    float M = m;
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+    float L = l * f;
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+    const int c = 2 * lane;
+    float O0 = 0.0f, O1 = 0.0f;
+    int s = 0;
+    for (; s + 16 <= S; s += 16) {
+      float2 ov[16];
+      float fv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        ov[j] = c < D ? *reinterpret_cast<const float2*>(apart_at(p, base + s + j, w, t) + c) : make_float2(0.f, 0.f);
+        fv[j] = __shfl(f, s + j);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        O0 = fmaf(ov[j].x, fv[j], O0);
+        O1 = fmaf(ov[j].y, fv[j], O1);
+      }
+    }
+    for (; s < S; ++s) {
+      const float fs = __shfl(f, s);
+      if (c < D) {
+        const float2 o2 = *reinterpret_cast<const float2*>(apart_at(p, base + s, w, t) + c);
+        O0 = fmaf(o2.x, fs, O0);
+        O1 = fmaf(o2.y, fs, O1);
+      }
+    }
+    if (c < D) {
+      const float out0 = O0 / L, out1 = O1 / L;
+      st_wt(reinterpret_cast<uint32_t*>(p.attn + (size_t)tok * Dq + h * D + c), pack2(f2h(out0), f2h(out1)));
+      if (debug) if (p.dbg.attn) {
+        p.dbg.attn[(size_t)tok * Dq + h * D + c] = out0;
+        p.dbg.attn[(size_t)tok * Dq + h * D + c + 1] = out1;
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Router: logit(t, e) = canonical fp32 dot of n2[t] and Wr[e] (lane j: fma
-// chain over k = j mod 64 ascending; then pairwise halving), plus bias.
-// One expert per workgroup (strided), one token per wave (strided).
+// Pooler input and router, from one pass over h1. For every token t:
+//   n2[k] = fl32(fl32(h1[k] * inv_rms[t]) * g[k])      (the fp32 router input)
+//   X[t][k] = fp16(n2[k])                               (the pooler's MFMA operand)
+//   logit(t, e) = tree(partials) + b[e], with partial j the fma chain over
+//   k = 8j .. 8j+7 ascending and the partials combined pairwise, adjacent
+//   pairs first.
+// Thread (t, j) owns elements 8j .. 8j+7 (H/8 divides the workgroup size), so
+// the first log2(64) tree levels are xor-shuffles and the rest go through
+// LDS. Workgroup w computes expert w's logits.
 // ---------------------------------------------------------------------------
-__device__ void router_phase(const Params& p, const Smem& sm, bool debug) {
-  const int lane = lane_id(), w = wave_id();
-  const int H = p.H;
-  for (int e = blockIdx.x; e < p.E; e += gridDim.x) {
-    const float* wr = p.cur.w_router + (size_t)e * H;
-    const float b = p.cur.b_router ? p.cur.b_router[e] : 0.0f;
-    for (int t = w; t < p.NT; t += kWaves) {
+__device__ __forceinline__ void fill_x_pool_router(const Params& p, Smem& sm) {
+  const int K = p.H, NT = p.NT, K8 = K / 8;
+  const int lane = lane_id();
+  const int e = blockIdx.x;
+  const bool route = e < p.E;
+  const int j8 = threadIdx.x % K8;
+  const int tstep = kThreads / K8;
+  const int nit = (kMaxTok + tstep - 1) / tstep;
+  const int inwave = K8 < 64 ? K8 : 64;
+  float* blk = &sm.red[0][0][0];  // [token][64-element block] sums when K8 > 64
+  float wv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (route) {
+    const float4* wp = reinterpret_cast<const float4*>(p.cur.w_router + (size_t)e * K + j8 * 8);
+    const float4 a = wp[0], b = wp[1];
+    wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w; wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
+  }
+  const float bias = (route && p.cur.b_router) ? p.cur.b_router[e] : 0.0f;
+  float gv[8];
+  {
+    const uint4 gg = *reinterpret_cast<const uint4*>(p.cur.g_moe + j8 * 8);
+    const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gv[j] = bf2f((uint16_t)(gw[j >> 1] >> ((j & 1) * 16)));
+  }
+  for (int it = 0; it < nit; ++it) {
+    const int t = threadIdx.x / K8 + it * tstep;
+    uint4 out = make_uint4(0, 0, 0, 0);
+    float acc = 0.0f;
+    if (t < NT) {
+      const float4* hp = reinterpret_cast<const float4*>(p.h1 + (size_t)t * K + j8 * 8);
+      const float4 a = hp[0], b = hp[1];
+      float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
       const float inv = sm.inv_rms[t];
-      const float* h = p.h1 + (size_t)t * H;
-      float acc = 0.0f;
-      for (int k = lane; k < H; k += 64) {
-        float x = h[k];
-        if (p.use_norm) x = (x * inv) * bf2f(p.cur.g_moe[k]);
-        acc = fmaf(x, wr[k], acc);
+      if (p.use_norm) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (v[j] * inv) * gv[j];
       }
-      for (int s = 32; s >= 1; s >>= 1) acc = acc + __shfl_xor(acc, s);
-      if (lane == 0) p.logits[(size_t)t * p.E + e] = acc + b;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = fmaf(v[j], wv[j], acc);
+      out.x = pack2(f2h(v[0]), f2h(v[1]));
+      out.y = pack2(f2h(v[2]), f2h(v[3]));
+      out.z = pack2(f2h(v[4]), f2h(v[5]));
+      out.w = pack2(f2h(v[6]), f2h(v[7]));
+    }
+    if (t < kMaxTok) *reinterpret_cast<uint4*>(sm.x + t * x_stride(K) + j8 * 16) = out;
+    if (route) {
+      for (int o = 1; o < inwave; o <<= 1) acc = acc + __shfl_xor(acc, o);
+      if (K8 <= 64) {
+        if (j8 == 0 && t < NT) st_wt(&p.logits[(size_t)t * p.E + e], acc + bias);
+      } else if (lane == 0 && t < kMaxTok) {
+        blk[t * 8 + j8 / 64] = acc;
+      }
     }
   }
-  if (debug && p.dbg.n2 && blockIdx.x == 0) {
-    for (int i = threadIdx.x; i < p.NT * H; i += kThreads) {
-      int t = i / H, k = i % H;
-      float x = p.h1[i];
-      if (p.use_norm) x = (x * sm.inv_rms[t]) * bf2f(p.cur.g_moe[k]);
-      p.dbg.n2[i] = x;
+  if (route && K8 > 64) {
+    __syncthreads();
+    if (threadIdx.x < NT) {
+      const int nblk = K8 / 64;  // 2, 4 or 8
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = q < nblk ? blk[threadIdx.x * 8 + q] : 0.0f;
+      const float a0 = v[0] + v[1], a1 = v[2] + v[3], a2 = v[4] + v[5], a3 = v[6] + v[7];
+      const float r = nblk == 2 ? a0 : (nblk == 4 ? a0 + a1 : (a0 + a1) + (a2 + a3));
+      st_wt(&p.logits[(size_t)threadIdx.x * p.E + e], r + bias);
     }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void dump_n2(const Params& p, const Smem& sm) {
+  for (int i = threadIdx.x; i < p.NT * p.H; i += kThreads) {
+    const int t = i / p.H, k = i % p.H;
+    float x = p.h1[i];
+    if (p.use_norm) x = (x * sm.inv_rms[t]) * bf2f(p.cur.g_moe[k]);
+    p.dbg.n2[i] = x;
   }
 }
 
@@ -695,6 +872,9 @@ struct Route {
   int32_t ids[kMaxTok][kMaxK];
   float gates[kMaxTok][kMaxK];
   float tokgate[kMaxTok * kMaxK][kMaxTok];  // [slot][token]
+  float ts_gu[kMaxTok * kMaxK];             // per selected slot: tensor scale of gate_up
+  float ts_dn[kMaxTok * kMaxK];             // ... and of down
+  int32_t count[kMaxE];                     // selections per expert (routing histogram)
   uint32_t mask[kMaxE / 32];
 };
 
@@ -704,11 +884,12 @@ static_assert(kRouteOff + (int)sizeof(Route) <= kXBytes, "route tables must fit 
 __device__ __forceinline__ Route& route_of(Smem& sm) { return *reinterpret_cast<Route*>(sm.x + kRouteOff); }
 
 // Top-k by (logit descending, index ascending); gates = softmax of the selected logits.
-__device__ void routing(const Params& p, Smem& sm, bool write_out) {
+__device__ __forceinline__ void routing(const Params& p, Smem& sm, bool write_out) {
   Route& rt = route_of(sm);
   const int lane = lane_id(), w = wave_id();
   const int E = p.E, K = p.topk;
   if (threadIdx.x < kMaxE / 32) rt.mask[threadIdx.x] = 0;
+  if (threadIdx.x < kMaxE) rt.count[threadIdx.x] = 0;
   __syncthreads();
   for (int t = w; t < p.NT; t += kWaves) {
     const float* lg = p.logits + (size_t)t * E;
@@ -753,6 +934,7 @@ __device__ void routing(const Params& p, Smem& sm, bool write_out) {
     int t = threadIdx.x / K, r = threadIdx.x % K;
     int e = rt.ids[t][r];
     atomicOr(&rt.mask[e >> 5], 1u << (e & 31));
+    atomicAdd(&rt.count[e], 1);
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -776,15 +958,16 @@ __device__ void routing(const Params& p, Smem& sm, bool write_out) {
         if (rt.ids[t][r] == rt.sel[j]) gv = rt.gates[t][r];
     rt.tokgate[j][t] = gv;
   }
+  for (int j = threadIdx.x; j < rt.n_sel; j += kThreads) {
+    rt.ts_gu[j] = p.cur.e_ts[2 * rt.sel[j]];
+    rt.ts_dn[j] = p.cur.e_ts[2 * rt.sel[j] + 1];
+  }
   if (write_out && threadIdx.x < p.NT * K) {
     int t = threadIdx.x / K, r = threadIdx.x % K;
     if (p.out_ids) p.out_ids[t * K + r] = rt.ids[t][r];
     if (p.out_gates) p.out_gates[t * K + r] = rt.gates[t][r];
   }
-  if (write_out && p.hist && threadIdx.x == 0) {
-    for (int t = 0; t < p.NT; ++t)
-      for (int r = 0; r < K; ++r) p.hist[(size_t)p.layer * E + rt.ids[t][r]] += 1;
-  }
+  if (write_out && p.hist && threadIdx.x < E) p.hist[(size_t)p.layer * E + threadIdx.x] = rt.count[threadIdx.x];
   __syncthreads();
 }
 
@@ -815,13 +998,17 @@ __device__ __forceinline__ void fp4_decode(uint4 codes, uint32_t sc2, uint4 out[
 // GEMM1: gate/up projection of the selected experts with SwiGLU.
 // Unit = (selected slot j, i-tile it): rows gate[it*8 .. +8) and up[I + it*8 .. +8)
 // as the 16 MFMA columns; k = P split over the waves in steps of 128
-// (lane group g holds the 32 elements at step*128 + g*32).
-struct G1Buf {
+// (lane group g holds the 32 elements at step*128 + g*32; wave w owns steps
+// w and w + 8). Steps beyond P load a clamped address and read the zero A
+// operand, so every unit issues the same loads (see the dense engine).
+constexpr int kG1Ring = 4;  // GEMM1 units whose loads are in flight per wave
+
+struct G1Slot {
   uint4 c[2];
   uint32_t s[2];
 };
 
-__device__ __forceinline__ void g1_load(const Params& p, const Route& rt, int u, G1Buf& b) {
+__device__ __forceinline__ void g1_issue(const Params& p, const Route& rt, int u, G1Slot& b) {
   const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4, w = wave_id();
   const int I = p.I, P = p.P, ntile = I / 8;
   const int j = u / ntile, it = u % ntile;
@@ -832,103 +1019,121 @@ __device__ __forceinline__ void g1_load(const Params& p, const Route& rt, int u,
   const int nsteps = P / 128;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    int st = w + c * kWaves;
-    if (st < nsteps) {
-      int k = st * 128 + g_ * 32;
-      b.c[c] = *reinterpret_cast<const uint4*>(codes + k / 2);
-      b.s[c] = *reinterpret_cast<const uint16_t*>(scs + k / 16);
+    const int st = w + c * kWaves;
+    const int k = (st < nsteps ? st : 0) * 128 + g_ * 32;
+    b.c[c] = *reinterpret_cast<const uint4*>(codes + k / 2);
+    b.s[c] = *reinterpret_cast<const uint16_t*>(scs + k / 16);
+  }
+}
+
+template <bool debug>
+__device__ __forceinline__ void g1_unit(const Params& p, Smem& sm, const Route& rt, int u, bool valid,
+                                        const G1Slot& cur, int rb) {
+  const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4, w = wave_id();
+  const int I = p.I, P = p.P, ntile = I / 8;
+  const int nsteps = P / 128;
+  const int j = u / ntile, it = u % ntile;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int st = w + c * kWaves;
+    const bool kv = st < nsteps;
+    uint4 bw[4];
+    fp4_decode(cur.c[c], cur.s[c], bw);
+    const int kbase = st * 128 + g_ * 32;
+    const uint8_t* abase = kv ? sm.x + r_ * x_stride(P) + kbase * 2 : reinterpret_cast<const uint8_t*>(&sm.zero);
+    const int astep = kv ? 16 : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = mfma_f16(*reinterpret_cast<const uint4*>(abase + q * astep), bw[q], acc);
+    if constexpr (debug) {
+      const int e = rt.sel[j];
+      if (valid && kv && p.dbg.dq_gu && e == p.dbg.dq_expert) {
+        const int row = r_ < 8 ? it * 8 + r_ : I + it * 8 + (r_ - 8);
+        uint4* dst = reinterpret_cast<uint4*>(p.dbg.dq_gu + (size_t)row * P + kbase);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = bw[q];
+      }
+    }
+  }
+  if (!valid) return;
+  red_store(sm, rb, acc);
+  __syncthreads();
+  if (threadIdx.x < kMaxTok * 4) {
+    const int tok = threadIdx.x >> 2, c = (threadIdx.x & 3) * 2;
+    if (tok < p.NT) {
+      const float ts = rt.ts_gu[j], tg = rt.tokgate[j][tok];
+      uint16_t out[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float gate = red_sum(sm, rb, tok * 16 + c + q) * ts;
+        float up = red_sum(sm, rb, tok * 16 + 8 + c + q) * ts;
+        float a = gate / (1.0f + expf(-gate)) * up;
+        out[q] = f2h(a * tg);
+      }
+      st_wt(reinterpret_cast<uint32_t*>(p.abuf + ((size_t)j * p.NT + tok) * I + it * 8 + c), pack2(out[0], out[1]));
     }
   }
 }
 
-__device__ void gemm1_phase(const Params& p, Smem& sm, bool debug) {
+template <bool debug>
+__device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
   Route& rt = route_of(sm);
-  const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4, w = wave_id();
-  const int I = p.I, P = p.P, ntile = I / 8;
+  const int ntile = p.I / 8;
   const int U = rt.n_sel * ntile;
   const int u0 = (int)((long long)blockIdx.x * U / gridDim.x);
   const int u1 = (int)((long long)(blockIdx.x + 1) * U / gridDim.x);
-  const int nsteps = P / 128;
-  G1Buf bA, bB;
-  if (u0 < u1) g1_load(p, rt, u0, bA);
+  if (u0 >= u1) return;
+  G1Slot ring[kG1Ring];
+#pragma unroll
+  for (int i = 0; i < kG1Ring; ++i) g1_issue(p, rt, min(u0 + i, u1 - 1), ring[i]);
   int rb = 0;
-  for (int u = u0; u < u1; ++u) {
-    G1Buf cur = bA;
-    if (u + 1 < u1) g1_load(p, rt, u + 1, bB);
-    const int j = u / ntile, it = u % ntile;
-    const int e = rt.sel[j];
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int base = u0; base < u1; base += kG1Ring) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      int st = w + c * kWaves;
-      if (st < nsteps) {
-        uint4 bw[4];
-        fp4_decode(cur.c[c], cur.s[c], bw);
-        const int kbase = st * 128 + g_ * 32;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint4 a = lds_x_read(sm, P, r_, kbase + q * 8);
-          acc = mfma_f16(a, bw[q], acc);
-        }
-        if (debug && p.dbg.dq_gu && e == p.dbg.dq_expert) {
-          const int row = r_ < 8 ? it * 8 + r_ : I + it * 8 + (r_ - 8);
-          uint4* dst = reinterpret_cast<uint4*>(p.dbg.dq_gu + (size_t)row * P + kbase);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) dst[q] = bw[q];
-        }
-      }
+    for (int i = 0; i < kG1Ring; ++i) {
+      const int uu = base + i;
+      const bool valid = uu < u1;
+      g1_unit<debug>(p, sm, rt, min(uu, u1 - 1), valid, ring[i], rb);
+      if (valid) rb ^= 1;
+      g1_issue(p, rt, min(uu + kG1Ring, u1 - 1), ring[i]);
     }
-    red_store(sm, rb, acc);
-    __syncthreads();
-    if (threadIdx.x < kMaxTok * 8) {
-      const int tok = threadIdx.x >> 3, c = threadIdx.x & 7;
-      if (tok < p.NT) {
-        const float ts = p.cur.e_ts[2 * e];
-        float gate = red_sum(sm, rb, tok * 16 + c) * ts;
-        float up = red_sum(sm, rb, tok * 16 + 8 + c) * ts;
-        float a = gate / (1.0f + expf(-gate)) * up;
-        a *= rt.tokgate[j][tok];
-        p.abuf[((size_t)j * p.NT + tok) * I + it * 8 + c] = f2h(a);
-      }
-    }
-    rb ^= 1;
-    bA = bB;
   }
   __syncthreads();
 }
 
 // GEMM2: down projection, summed over a contiguous range of selected experts.
-// Workgroup = (row tile of 16 of P, expert part); k = I split over the waves
-// in steps of 128; per expert the fp32 tensor scale is applied to the MFMA
-// partial before it is added to the running sum.
-struct G2Buf {
+// Workgroup = (row tile of 16 of P, expert part); wave w owns k in
+// [w*128, w*128+128) of I (lane group g: 32 elements at w*128 + g*32). The A
+// operand of a token not routed to the expert (or of k beyond I) is read from
+// a zero line in the workspace, so every expert issues the same loads. Per
+// expert the fp32 tensor scale is applied to the MFMA partial before it is
+// added to the running sum.
+constexpr int kG2Ring = 4;  // GEMM2 experts whose loads are in flight per wave
+
+struct G2Slot {
   uint4 c;
   uint32_t s;
   uint4 a[4];
 };
 
-__device__ __forceinline__ void g2_load(const Params& p, const Route& rt, int j, int tile, G2Buf& b) {
+__device__ __forceinline__ void g2_issue(const Params& p, const Route& rt, int j, int tile, G2Slot& b) {
   const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4, w = wave_id();
   const int I = p.I, P = p.P;
   const int e = rt.sel[j];
   const int k = w * 128 + g_ * 32;
+  const bool kv = k < I;
+  const int kk = kv ? k : 0;
   const int row = tile * 16 + r_;
-  b.c = make_uint4(0, 0, 0, 0);
-  b.s = 0;
-  if (k < I) {
-    b.c = *reinterpret_cast<const uint4*>(p.cur.e_dn + (size_t)e * P * (I / 2) + (size_t)row * (I / 2) + k / 2);
-    b.s = *reinterpret_cast<const uint16_t*>(p.cur.e_dn_sc + (size_t)e * P * (I / 16) + (size_t)row * (I / 16) + k / 16);
-  }
+  b.c = *reinterpret_cast<const uint4*>(p.cur.e_dn + (size_t)e * P * (I / 2) + (size_t)row * (I / 2) + kk / 2);
+  b.s = *reinterpret_cast<const uint16_t*>(p.cur.e_dn_sc + (size_t)e * P * (I / 16) + (size_t)row * (I / 16) + kk / 16);
+  const bool routed = kv && r_ < p.NT && rt.tokgate[j][r_] != 0.0f;
+  const uint16_t* src = routed ? p.abuf + ((size_t)j * p.NT + r_) * I + k : p.zeros;
+  const int step = routed ? 8 : 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) b.a[q] = make_uint4(0, 0, 0, 0);
-  if (k < I && r_ < p.NT && rt.tokgate[j][r_] != 0.0f) {
-    const uint4* src = reinterpret_cast<const uint4*>(p.abuf + ((size_t)j * p.NT + r_) * I + k);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) b.a[q] = src[q];
-  }
+  for (int q = 0; q < 4; ++q) b.a[q] = *reinterpret_cast<const uint4*>(src + q * step);
 }
 
-__device__ void gemm2_phase(const Params& p, Smem& sm, bool debug) {
+template <bool debug>
+__device__ __forceinline__ void gemm2_phase(const Params& p, Smem& sm) {
   Route& rt = route_of(sm);
   const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4, w = wave_id();
   const int I = p.I, P = p.P;
@@ -937,38 +1142,43 @@ __device__ void gemm2_phase(const Params& p, Smem& sm, bool debug) {
   if ((int)blockIdx.x >= tiles * parts) return;
   const int tile = blockIdx.x % tiles, part = blockIdx.x / tiles;
   const int j0 = part * rt.n_sel / parts, j1 = (part + 1) * rt.n_sel / parts;
-  const bool kact = w * 128 < I;
   f32x4_t total = {0.f, 0.f, 0.f, 0.f};
-  G2Buf bA, bB;
-  if (j0 < j1) g2_load(p, rt, j0, tile, bA);
-  for (int j = j0; j < j1; ++j) {
-    G2Buf cur = bA;
-    if (j + 1 < j1) g2_load(p, rt, j + 1, tile, bB);
-    if (kact) {
-      const int e = rt.sel[j];
-      uint4 bw[4];
-      fp4_decode(cur.c, cur.s, bw);
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (j0 < j1) {
+    G2Slot ring[kG2Ring];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc = mfma_f16(cur.a[q], bw[q], acc);
-      const float ts = p.cur.e_ts[2 * e + 1];
+    for (int i = 0; i < kG2Ring; ++i) g2_issue(p, rt, min(j0 + i, j1 - 1), tile, ring[i]);
+    for (int base = j0; base < j1; base += kG2Ring) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) total[i] = fmaf(acc[i], ts, total[i]);
-      if (debug && p.dbg.dq_dn && e == p.dbg.dq_expert) {
-        const int k = w * 128 + g_ * 32;
-        uint4* dst = reinterpret_cast<uint4*>(p.dbg.dq_dn + (size_t)(tile * 16 + r_) * I + k);
-        const int nq = min(4, (I - k) / 8);
-        for (int q = 0; q < nq; ++q) dst[q] = bw[q];
+      for (int i = 0; i < kG2Ring; ++i) {
+        const int jj = base + i;
+        const int jc = min(jj, j1 - 1);
+        uint4 bw[4];
+        fp4_decode(ring[i].c, ring[i].s, bw);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = mfma_f16(ring[i].a[q], bw[q], acc);
+        const float ts = jj < j1 ? rt.ts_dn[jc] : 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) total[c] = fmaf(acc[c], ts, total[c]);
+        if constexpr (debug) {
+          const int e = rt.sel[jc];
+          const int k = w * 128 + g_ * 32;
+          if (jj < j1 && k < I && p.dbg.dq_dn && e == p.dbg.dq_expert) {
+            uint4* dst = reinterpret_cast<uint4*>(p.dbg.dq_dn + (size_t)(tile * 16 + r_) * I + k);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dst[q] = bw[q];
+          }
+        }
+        g2_issue(p, rt, min(jj + kG2Ring, j1 - 1), tile, ring[i]);
       }
     }
-    bA = bB;
   }
   red_store(sm, 0, total);
   __syncthreads();
   if (threadIdx.x < 256) {
     const int tok = threadIdx.x >> 4, row = threadIdx.x & 15;
     float v = red_sum(sm, 0, threadIdx.x);
-    if (tok < p.NT) p.accpart[((size_t)part * p.NT + tok) * P + tile * 16 + row] = v;
+    if (tok < p.NT) st_wt(&p.accpart[((size_t)part * p.NT + tok) * P + tile * 16 + row], v);
   }
   __syncthreads();
 }
@@ -976,22 +1186,46 @@ __device__ void gemm2_phase(const Params& p, Smem& sm, bool debug) {
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-template <uint32_t MODE, bool DEBUG>
+// Phase-boundary slots of the self-timing trace (one uint64 per slot, per
+// workgroup, per launch; 100 MHz real-time counter).
+enum TraceSlot {
+  kTrStart = 0, kTrQkvOwn, kTrQkvOwnBar, kTrAttn, kTrAttnBar, kTrMerge, kTrMergeBar, kTrOproj,
+  kTrOprojBar, kTrRouterPool, kTrRouterPoolBar, kTrGemm1, kTrGemm1Bar, kTrGemm2, kTrGemm2Bar,
+  kTrUnpool, kTrUnpoolBar, kTrQkvNext, kTrSlots
+};
+static_assert(kTrSlots == kTraceSlots, "trace slot count");
+
+enum Variant { kPlain = 0, kDebug = 1, kTrace = 2 };
+
+template <uint32_t MODE, int VARIANT>
 __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
+  constexpr bool DEBUG = VARIANT == kDebug;
+  constexpr bool TRACE = VARIANT == kTrace;
   __shared__ Smem sm;
-  Barrier bar{p.bar, p.err, (p.bar_base + 1) * gridDim.x, gridDim.x};
+  Barrier bar{p.bar, p.err, p.bar_base + 1};
+  uint64_t* const trace_row = TRACE ? p.trace + ((size_t)p.trace_launch * kMaxGrid + blockIdx.x) * kTraceSlots : nullptr;
+  auto mark = [trace_row](int slot) {
+    if constexpr (TRACE) {
+      if (threadIdx.x == 0) trace_row[slot] = __builtin_amdgcn_s_memrealtime();
+    }
+  };
+  mark(kTrStart);
   const int Dq = p.nq * p.d;
   const int Nqkv = Dq + 2 * p.nkv * p.d;
-  DenseBuf pre;
+  DenseSlot ring[kRing];
+  if (threadIdx.x == 0) sm.zero = make_uint4(0, 0, 0, 0);
 
   if constexpr ((MODE & kModeQkvOwn) != 0) {
-    dense_prefetch(p.s_qkv_own, p.cur.w_qkv, p.H, pre);
+    dense_prefetch<Epi::Qkv>(p, p.s_qkv_own, p.cur.w_qkv, p.H, nullptr, ring);
     compute_inv_rms(p, p.h_in, nullptr, sm);
-    fill_x_norm(p, p.h_in, p.cur.g_attn, sm);
-    EpiArgs ea{&p.cur, nullptr, p.qpart, nullptr, DEBUG ? p.dbg.k_new : nullptr, DEBUG ? p.dbg.v_new : nullptr};
-    dense_phase<Epi::Qkv>(p, p.s_qkv_own, p.cur.w_qkv, p.H, p.H, ea, sm, pre, true);
+    fill_x_norm(p, p.h_in, p.cur.g_attn, sm, false);
+    EpiArgs ea{p.cur.k_cache, p.cur.v_cache, nullptr, p.qpart, nullptr, DEBUG ? p.dbg.k_new : nullptr,
+               DEBUG ? p.dbg.v_new : nullptr};
+    dense_phase<Epi::Qkv>(p, p.s_qkv_own, p.cur.w_qkv, p.H, p.H, ea, sm, ring);
+    mark(kTrQkvOwn);
     bar_arrive(bar);
     if (!bar_wait(bar, sm)) return;
+    mark(kTrQkvOwnBar);
     if (DEBUG && p.dbg.q) {
       for (int i = blockIdx.x * kThreads + threadIdx.x; i < p.NT * Dq; i += gridDim.x * kThreads) {
         float v = 0.0f;
@@ -1005,23 +1239,29 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   // attention of the launch's layer
   if (p.d == 128) attention_phase<128>(p, p.cur, sm);
   else attention_phase<64>(p, p.cur, sm);
+  mark(kTrAttn);
   bar_arrive(bar);
   if (!bar_wait(bar, sm)) return;
+  mark(kTrAttnBar);
 
-  merge_phase(p, p.cur, DEBUG);
+  merge_phase<DEBUG>(p, p.cur);
+  mark(kTrMerge);
   bar_arrive(bar);
-  dense_prefetch(p.s_oproj, p.cur.w_o, Dq, pre);
+  dense_prefetch<Epi::OProj>(p, p.s_oproj, p.cur.w_o, Dq, p.h_in, ring);
   if (!bar_wait(bar, sm)) return;
+  mark(kTrMergeBar);
 
   // output projection + residual
   {
     fill_x_copy(p.attn, Dq, p.NT, sm);
-    EpiArgs ea{nullptr, p.h_in, p.h1, p.ssq1, nullptr, nullptr};
-    dense_phase<Epi::OProj>(p, p.s_oproj, p.cur.w_o, Dq, Dq, ea, sm, pre, true);
+    EpiArgs ea{nullptr, nullptr, p.h_in, p.h1, p.ssq1, nullptr, nullptr};
+    dense_phase<Epi::OProj>(p, p.s_oproj, p.cur.w_o, Dq, Dq, ea, sm, ring);
   }
+  mark(kTrOproj);
   bar_arrive(bar);
-  dense_prefetch(p.s_pool, p.cur.w_pool, p.H, pre);
+  dense_prefetch<Epi::Pool>(p, p.s_pool, p.cur.w_pool, p.H, nullptr, ring);
   if (!bar_wait(bar, sm)) return;
+  mark(kTrOprojBar);
   if (DEBUG && p.dbg.h1) {
     for (int i = blockIdx.x * kThreads + threadIdx.x; i < p.NT * p.H; i += gridDim.x * kThreads) p.dbg.h1[i] = p.h1[i];
   }
@@ -1029,13 +1269,15 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   // router + pooler (both read n2 = RMSNorm(h1))
   {
     compute_inv_rms(p, p.h1, p.ssq1, sm);
-    fill_x_norm(p, p.h1, p.cur.g_moe, sm);
-    EpiArgs ea{nullptr, nullptr, p.ppart, nullptr, nullptr, nullptr};
-    dense_phase<Epi::Pool>(p, p.s_pool, p.cur.w_pool, p.H, p.H, ea, sm, pre, true);
-    router_phase(p, sm, DEBUG);
+    fill_x_pool_router(p, sm);
+    if (DEBUG && p.dbg.n2 && blockIdx.x == 0) dump_n2(p, sm);
+    EpiArgs ea{nullptr, nullptr, nullptr, p.ppart, nullptr, nullptr, nullptr};
+    dense_phase<Epi::Pool>(p, p.s_pool, p.cur.w_pool, p.H, p.H, ea, sm, ring);
   }
+  mark(kTrRouterPool);
   bar_arrive(bar);
   if (!bar_wait(bar, sm)) return;
+  mark(kTrRouterPoolBar);
 
   // routing (every workgroup) + experts' gate/up
   fill_x_sum(p.ppart, p.p_slices, p.P, p.NT, sm);
@@ -1050,21 +1292,25 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
         p.dbg.p[i] = v;
       }
   }
-  gemm1_phase(p, sm, DEBUG);
+  gemm1_phase<DEBUG>(p, sm);
+  mark(kTrGemm1);
   bar_arrive(bar);
   if (!bar_wait(bar, sm)) return;
+  mark(kTrGemm1Bar);
 
-  gemm2_phase(p, sm, DEBUG);
+  gemm2_phase<DEBUG>(p, sm);
+  mark(kTrGemm2);
   bar_arrive(bar);
-  dense_prefetch(p.s_unpool, p.cur.w_unpool, p.P, pre);
+  dense_prefetch<Epi::Unpool>(p, p.s_unpool, p.cur.w_unpool, p.P, p.h1, ring);
   if (!bar_wait(bar, sm)) return;
+  mark(kTrGemm2Bar);
 
   // unpooler + residual
   {
     const int parts = max(1, (int)gridDim.x / (p.P / 16));
     fill_x_sum(p.accpart, parts, p.P, p.NT, sm);
-    EpiArgs ea{nullptr, p.h1, p.h_out, p.ssq2, nullptr, nullptr};
-    dense_phase<Epi::Unpool>(p, p.s_unpool, p.cur.w_unpool, p.P, p.P, ea, sm, pre, true);
+    EpiArgs ea{nullptr, nullptr, p.h1, p.h_out, p.ssq2, nullptr, nullptr};
+    dense_phase<Epi::Unpool>(p, p.s_unpool, p.cur.w_unpool, p.P, p.P, ea, sm, ring);
     if (DEBUG && p.dbg.acc && blockIdx.x == 0) {
       for (int i = threadIdx.x; i < p.NT * p.P; i += kThreads) {
         float v = 0.0f;
@@ -1074,47 +1320,53 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
     }
   }
 
+  mark(kTrUnpool);
   if constexpr ((MODE & kModeQkvNext) != 0) {
     bar_arrive(bar);
-    dense_prefetch(p.s_qkv_next, p.nxt.w_qkv, p.H, pre);
+    dense_prefetch<Epi::Qkv>(p, p.s_qkv_next, p.nxt.w_qkv, p.H, nullptr, ring);
     if (!bar_wait(bar, sm)) return;
-    compute_inv_rms(p, p.h_out, p.ssq2, sm);
-    fill_x_norm(p, p.h_out, p.nxt.g_attn, sm);
-    EpiArgs ea{&p.nxt, nullptr, p.qpart, nullptr, nullptr, nullptr};
-    dense_phase<Epi::Qkv>(p, p.s_qkv_next, p.nxt.w_qkv, p.H, p.H, ea, sm, pre, true);
+    mark(kTrUnpoolBar);
+    fill_x_qkv(p, p.h_out, p.nxt.g_attn, p.ssq2, sm);
+    EpiArgs ea{p.nxt.k_cache, p.nxt.v_cache, nullptr, p.qpart, nullptr, nullptr, nullptr};
+    dense_phase<Epi::Qkv>(p, p.s_qkv_next, p.nxt.w_qkv, p.H, p.H, ea, sm, ring);
+    mark(kTrQkvNext);
   }
 }
 
 __global__ void reset_kernel(uint32_t* bar, int32_t* err) {
-  if (threadIdx.x == 0) {
-    *bar = 0;
-    *err = 0;
-  }
+  if (threadIdx.x < kMaxGrid) bar[threadIdx.x] = 0;
+  if (threadIdx.x == 0) *err = 0;
 }
 
 }  // namespace
 }  // namespace msk
 
-hipError_t msk_launch_layer(const msk::Params& p, int grid, bool debug, hipStream_t s) {
+template <int V>
+static hipError_t launch_mode(const msk::Params& p, dim3 g, dim3 b, hipStream_t s) {
   using namespace msk;
-  const uint32_t mode = p.mode;
-  dim3 g(grid), b(kThreads);
-  if (debug) {
-    if (mode != kModeQkvOwn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((layer_kernel<kModeQkvOwn, true>), g, b, 0, s, p);
-  } else if (mode == kModeQkvOwn) {
-    hipLaunchKernelGGL((layer_kernel<kModeQkvOwn, false>), g, b, 0, s, p);
-  } else if (mode == (kModeQkvOwn | kModeQkvNext)) {
-    hipLaunchKernelGGL((layer_kernel<kModeQkvOwn | kModeQkvNext, false>), g, b, 0, s, p);
-  } else if (mode == kModeQkvNext) {
-    hipLaunchKernelGGL((layer_kernel<kModeQkvNext, false>), g, b, 0, s, p);
-  } else {
-    hipLaunchKernelGGL((layer_kernel<0u, false>), g, b, 0, s, p);
+  switch (p.mode) {
+    case kModeQkvOwn: hipLaunchKernelGGL((layer_kernel<kModeQkvOwn, V>), g, b, 0, s, p); break;
+    case kModeQkvOwn | kModeQkvNext:
+      hipLaunchKernelGGL((layer_kernel<kModeQkvOwn | kModeQkvNext, V>), g, b, 0, s, p); break;
+    case kModeQkvNext: hipLaunchKernelGGL((layer_kernel<kModeQkvNext, V>), g, b, 0, s, p); break;
+    default: hipLaunchKernelGGL((layer_kernel<0u, V>), g, b, 0, s, p); break;
   }
   return hipGetLastError();
 }
 
+hipError_t msk_launch_layer(const msk::Params& p, int grid, bool debug, hipStream_t s) {
+  using namespace msk;
+  dim3 g(grid), b(kThreads);
+  if (debug) {
+    if (p.mode != kModeQkvOwn) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((layer_kernel<kModeQkvOwn, kDebug>), g, b, 0, s, p);
+    return hipGetLastError();
+  }
+  if (p.trace) return launch_mode<kTrace>(p, g, b, s);
+  return launch_mode<kPlain>(p, g, b, s);
+}
+
 hipError_t msk_launch_reset(uint32_t* bar, int32_t* err, hipStream_t s) {
-  hipLaunchKernelGGL(msk::reset_kernel, dim3(1), dim3(64), 0, s, bar, err);
+  hipLaunchKernelGGL(msk::reset_kernel, dim3(1), dim3(msk::kMaxGrid), 0, s, bar, err);
   return hipGetLastError();
 }

@@ -46,7 +46,13 @@ class msk_debug(ctypes.Structure):
 class msk_io(ctypes.Structure):
     _fields_ = [("n_requests", i32), ("n_tokens", i32), ("ctx_len", ctypes.POINTER(i32)),
                 ("h_in", vp), ("h_out", vp), ("expert_ids", vp), ("gates", vp),
-                ("debug", ctypes.POINTER(msk_debug))]
+                ("debug", ctypes.POINTER(msk_debug)), ("trace", vp)]
+
+
+TRACE_SLOTS = ["start", "qkv_own", "qkv_own_bar", "attn", "attn_bar", "merge", "merge_bar", "oproj",
+               "oproj_bar", "router_pool", "router_pool_bar", "gemm1", "gemm1_bar", "gemm2", "gemm2_bar",
+               "unpool", "unpool_bar", "qkv_next"]
+MAX_GRID = 256
 
 
 _lib = None
@@ -140,11 +146,11 @@ def make_layer_desc(t: Dict, window: int) -> msk_layer_desc:
 
 
 def make_io(n_requests, n_tokens, ctx: Sequence[int], h_in, h_out, expert_ids=None, gates=None,
-            debug: Optional[msk_debug] = None):
+            debug: Optional[msk_debug] = None, trace=None):
     ctx_arr = (i32 * len(ctx))(*ctx)
     io = msk_io(n_requests=n_requests, n_tokens=n_tokens, ctx_len=ctypes.cast(ctx_arr, ctypes.POINTER(i32)),
                 h_in=_ptr(h_in), h_out=_ptr(h_out), expert_ids=_ptr(expert_ids), gates=_ptr(gates),
-                debug=ctypes.pointer(debug) if debug is not None else None)
+                debug=ctypes.pointer(debug) if debug is not None else None, trace=_ptr(trace))
     io._keep = (ctx_arr, debug)
     return io
 

@@ -282,3 +282,64 @@ def to_device(arrays: dict, device="cuda") -> dict:
             t = torch.from_numpy(np.ascontiguousarray(a))
         out[name] = t.to(device)
     return out
+
+
+def device_layer(w: Workload, layer: int, device="cuda", with_cache=True, stream_ptr=None) -> dict:
+    """One layer's weights (and KV caches) filled directly in device memory by
+    the device filler: the same bytes layer_weights()/kv_cache() produce."""
+    import torch
+    s = w.seed
+    Nqkv = w.Dq + 2 * w.Dkv
+    i16 = dict(dtype=torch.int16, device=device)
+    u8 = dict(dtype=torch.uint8, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    t = {
+        "w_qkv": torch.empty((Nqkv, w.H), **i16),
+        "w_o": torch.empty((w.H, w.Dq), **i16),
+        "w_router": torch.empty((w.E, w.H), **f32),
+        "w_pool": torch.empty((w.P, w.H), **i16),
+        "w_unpool": torch.empty((w.H, w.P), **i16),
+        "g_attn": torch.full((w.H,), BF16_ONE, **i16),
+        "g_moe": torch.full((w.H,), BF16_ONE, **i16),
+        "e_gate_up": torch.empty((w.E, 2 * w.I, w.P // 2), **u8),
+        "e_gate_up_scale": torch.empty((w.E, 2 * w.I, w.P // 16), **u8),
+        "e_down": torch.empty((w.E, w.P, w.I // 2), **u8),
+        "e_down_scale": torch.empty((w.E, w.P, w.I // 16), **u8),
+    }
+    dev_normal_bf16(t["w_qkv"], s, stream_id(layer, W_QKV), WEIGHT_STD, stream_ptr)
+    dev_normal_bf16(t["w_o"], s, stream_id(layer, W_O), WEIGHT_STD, stream_ptr)
+    dev_normal_f32(t["w_router"], s, stream_id(layer, W_ROUTER), WEIGHT_STD, stream_ptr)
+    dev_normal_bf16(t["w_pool"], s, stream_id(layer, W_POOL), WEIGHT_STD, stream_ptr)
+    dev_normal_bf16(t["w_unpool"], s, stream_id(layer, W_UNPOOL), WEIGHT_STD, stream_ptr)
+    for e in range(w.E):
+        dev_nvfp4(t["e_gate_up"][e], t["e_gate_up_scale"][e], 2 * w.I, w.P, s,
+                  stream_id(layer, E_GATE_UP, e), WEIGHT_STD, w.gu_scale, stream_ptr)
+        dev_nvfp4(t["e_down"][e], t["e_down_scale"][e], w.P, w.I, s,
+                  stream_id(layer, E_DOWN, e), WEIGHT_STD, w.dn_scale, stream_ptr)
+    t["e_tensor_scale"] = torch.from_numpy(
+        np.tile(np.array([w.gu_scale, w.dn_scale], np.float32), (w.E, 1))).to(device)
+    t["b_router"] = (torch.from_numpy(zipf_bias(w.E, s, stream_id(layer, ROUTER_PERM), w.zipf_s)).to(device)
+                     if w.zipf_s else None)
+    if with_cache:
+        k = torch.empty((w.R, w.nkv, w.cap, w.d), **i16)
+        v = torch.empty((w.R, w.nkv, w.cap, w.d), **i16)
+        for r in range(w.R):
+            dev_normal_bf16(k[r], s, stream_id(layer, K_CACHE, r), 1.0, stream_ptr)
+            dev_normal_bf16(v[r], s, stream_id(layer, V_CACHE, r), 1.0, stream_ptr)
+        t["k_cache"], t["v_cache"] = k, v
+    return t
+
+
+def algorithmic_bytes_per_layer(w: Workload, layer: int, n_sel: int) -> int:
+    """Bytes the layer must move (each once): dense weights, the selected
+    experts' codes and scales, the KV rows in the union of the verify tokens'
+    windows, and the KV write. Unselected experts and out-of-window rows are
+    not counted."""
+    Nqkv = w.Dq + 2 * w.Dkv
+    dense = 2 * (Nqkv * w.H + w.H * w.Dq + w.P * w.H + w.H * w.P) + 4 * w.E * w.H + 2 * 2 * w.H
+    expert = (2 * w.I * w.P) // 2 + (2 * w.I * w.P) // 16 + (w.P * w.I) // 2 + (w.P * w.I) // 16 + 8
+    win = w.windows[layer]
+    rows = (w.ctx + w.T) if win <= 0 else min(w.ctx + w.T, win + w.T - 1)
+    kv_read = w.R * rows * w.nkv * w.d * 2 * 2
+    kv_write = w.R * w.T * w.nkv * w.d * 2 * 2
+    return dense + n_sel * expert + kv_read + kv_write
