@@ -38,10 +38,59 @@ def parse():
     ap.add_argument("--workload", default="step62",
                     choices=["step62", "swa_layer", "global_layer", "tiny_swa"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", default="0,3", help="layers of the step the oracle times")
+    ap.add_argument("--cpu-layers", default="0,1,2,3,4,5,6,7", help="layers of the step the oracle times")
     ap.add_argument("--trace", action="store_true",
                     help="after timing, run one step with the self-timing kernel and print the phase breakdown")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the reference kernel that "
+                         "scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_kernel_step62_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "moe_decode_megakernel_amd", "csrc", n)
+                  for n in ("msk_layer.hip", "msk_internal.h", "msk_api.cpp")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per layer launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by the copy calibration), or None when
+    the summary is missing or was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+    if kv.get("kernel_sources_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 28  # fp32 elements: 1 GiB
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n, "copies": 3}), flush=True)
 
 
 def main():
@@ -57,6 +106,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     w = synth.WORKLOADS[args.workload]
     dev = "cuda"
     stream = torch.cuda.current_stream()
@@ -161,7 +213,8 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "msk layer_kernel (one launch per layer boundary)",
             "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic() if w.name == "step62" else None,
             "bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(avg_launch_us, 2),
         },
     }

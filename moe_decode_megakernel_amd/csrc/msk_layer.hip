@@ -9,10 +9,10 @@
 // layer's own QKV projection and KV write.
 //
 // Execution model: one workgroup of 8 waves per compute unit, resident for
-// the whole launch. Phases are separated by a grid barrier (one counter in
-// the workspace, release/acquire at agent scope, bounded spin). Weight tiles
-// of the next phase are requested before waiting on the barrier, so the
-// barrier latency overlaps the first weight fetch. Every contraction runs on
+// the whole launch. Phases are separated by a grid barrier (a sequence-number
+// flag per workgroup, bounded spin; see Barrier below). Weight tiles of the
+// next phase are requested before waiting on the barrier, so the barrier
+// latency overlaps the first weight fetch. Every contraction runs on
 // fp16 MFMA (16x16x32, fp32 accumulation) with the 16 verify tokens as one
 // 16-row tile: bf16 weights and cache rows convert to fp16 exactly (in fp16's
 // normal range), activations are rounded to fp16 (11-bit significand), and
