@@ -136,12 +136,15 @@ typedef struct {
                              does not reach are left untouched. Exclusive with debug. */
 } msk_io;
 
-/* Trace slots, in execution order ("_BAR" = after the grid barrier that follows). */
+/* Trace slots, in execution order ("_BAR" = after the grid barrier that
+ * follows; "_FILL" = after the phase's activation tile is in LDS; ROUTING =
+ * after top-k and the routing tables). */
 enum {
   MSK_TR_START = 0, MSK_TR_QKV_OWN, MSK_TR_QKV_OWN_BAR, MSK_TR_ATTN, MSK_TR_ATTN_BAR,
-  MSK_TR_MERGE, MSK_TR_MERGE_BAR, MSK_TR_OPROJ, MSK_TR_OPROJ_BAR, MSK_TR_ROUTER_POOL,
-  MSK_TR_ROUTER_POOL_BAR, MSK_TR_GEMM1, MSK_TR_GEMM1_BAR, MSK_TR_GEMM2, MSK_TR_GEMM2_BAR,
-  MSK_TR_UNPOOL, MSK_TR_UNPOOL_BAR, MSK_TR_QKV_NEXT, MSK_TRACE_SLOTS
+  MSK_TR_MERGE, MSK_TR_MERGE_BAR, MSK_TR_OPROJ_FILL, MSK_TR_OPROJ, MSK_TR_OPROJ_BAR,
+  MSK_TR_POOL_FILL, MSK_TR_ROUTER_POOL, MSK_TR_ROUTER_POOL_BAR, MSK_TR_ROUTING, MSK_TR_GEMM1,
+  MSK_TR_GEMM1_BAR, MSK_TR_GEMM2, MSK_TR_GEMM2_BAR, MSK_TR_UNPOOL_FILL, MSK_TR_UNPOOL,
+  MSK_TR_UNPOOL_BAR, MSK_TR_QKV_FILL, MSK_TR_QKV_NEXT, MSK_TRACE_SLOTS
 };
 
 /* Bytes of device workspace a handle needs for this configuration; 0 if the

@@ -108,7 +108,7 @@ struct msk_handle_s {
   std::vector<msk_layer_desc> layers;
   std::vector<bool> loaded;
   int q_slices = 1, p_slices = 1;
-  msk::Sched s_qkv{}, s_oproj{}, s_pool{}, s_unpool{};
+  msk::Sched sched[msk::kSchCount]{};
   int32_t* err_host = nullptr;
   std::string last_error;
 };
@@ -204,6 +204,13 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
     return fail(nullptr, MSK_E_HIP, "no HIP device");
   const int G = std::min(prop.multiProcessorCount, kMaxGrid);
   if (cfg->n_experts > G) return fail(nullptr, MSK_E_SHAPE, "n_experts exceeds the workgroups of one launch (one router expert per workgroup)");
+  {
+    // GEMM1 stages 256 B per (selected expert, 8-row i-tile) unit of a workgroup in LDS
+    const int64_t nsel = std::min<int64_t>(cfg->n_experts, (int64_t)cfg->max_tokens * cfg->max_requests * cfg->top_k);
+    const int64_t units = nsel * (cfg->expert_inter / 8);
+    if ((units + G - 1) / G * 256 > msk::kG1StageBytes)
+      return fail(nullptr, MSK_E_SHAPE, "too many expert units per workgroup for the GEMM1 staging area");
+  }
   Layout lay = make_layout(cfg, kMaxGrid);
   if (bytes < lay.total) return fail(nullptr, MSK_E_CAPACITY, "workspace smaller than msk_workspace_bytes");
 
@@ -241,10 +248,16 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
     dst.units = reinterpret_cast<const msk::Unit*>(h->ws + lay.sched + at);
     dst.off = reinterpret_cast<const int32_t*>(h->ws + lay.sched + at2);
   };
-  put(sq, h->s_qkv);
-  put(so, h->s_oproj);
-  put(sp, h->s_pool);
-  put(su, h->s_unpool);
+  const SchedHost* all[msk::kSchCount] = {&sq, &so, &sp, &su};
+  for (int i = 0; i < msk::kSchCount; ++i) {
+    for (int g = 0; g < G; ++g) {
+      if (all[i]->off[g + 1] - all[i]->off[g] > msk::kMaxWgUnits) {
+        delete h;
+        return fail(nullptr, MSK_E_SHAPE, "a dense schedule gives one workgroup more units than it stages");
+      }
+    }
+    put(*all[i], h->sched[i]);
+  }
   if (blob.size() > lay.h1 - lay.sched) {
     delete h;
     return fail(nullptr, MSK_E_CAPACITY, "schedule tables exceed their workspace region");
@@ -375,11 +388,7 @@ msk::Params base_params(msk_handle h, const msk_io* io) {
   p.accpart = reinterpret_cast<float*>(ws + L.accpart);
   p.hist = reinterpret_cast<int32_t*>(ws + L.hist);
   p.zeros = reinterpret_cast<const uint16_t*>(ws + L.zeros);
-  p.s_qkv_own = h->s_qkv;
-  p.s_qkv_next = h->s_qkv;
-  p.s_oproj = h->s_oproj;
-  p.s_pool = h->s_pool;
-  p.s_unpool = h->s_unpool;
+  for (int i = 0; i < msk::kSchCount; ++i) p.sched[i] = h->sched[i];
   return p;
 }
 

@@ -18,7 +18,11 @@ constexpr int kMaxK = 8;
 constexpr int kMaxHeadDim = 128;
 constexpr int kSubK = 128;                // dense k per wave sub-unit (4 MFMA steps of 32)
 constexpr int kAttnChunk = 64;            // keys per attention chunk in LDS
-constexpr int kTraceSlots = 18;           // phase-boundary timestamps per workgroup per launch
+constexpr int kTraceSlots = 23;            // phase-boundary timestamps per workgroup per launch
+constexpr int kG1StageBytes = 32768;       // LDS staging of GEMM1 outputs per workgroup (256 B per unit)
+constexpr int kMaxWgUnits = 32;            // dense units of one workgroup in one schedule
+constexpr int kMaxQSlices = 4;             // split-K slices of the Q projection
+constexpr int kMaxSplits = 64;             // attention splits per (request, kv head)
 
 // Launch modes (bit set).
 enum : uint32_t {
@@ -72,6 +76,8 @@ struct Debug {
 };
 
 // Schedules of the dense phases (CSR over workgroups), built once per handle.
+// A workgroup's units of every schedule are copied to LDS at launch start.
+enum { kSchQkv = 0, kSchOproj, kSchPool, kSchUnpool, kSchCount };
 struct Sched {
   const Unit* units;
   const int32_t* off;  // [G + 1]
@@ -106,7 +112,7 @@ struct Params {
   float* accpart;         // [parts][NT][P]
   int32_t* hist;          // [n_layers][E] selection counts
   const uint16_t* zeros;  // 256 zero bytes (A operand of masked lanes)
-  Sched s_qkv_own, s_qkv_next, s_oproj, s_pool, s_unpool;
+  Sched sched[kSchCount];  // QKV (own and next layer share shapes), O proj, pool, unpool
   // outputs
   int32_t* out_ids;       // [NT][k] or NULL
   float* out_gates;

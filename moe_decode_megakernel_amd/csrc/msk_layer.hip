@@ -43,6 +43,8 @@ struct Smem {
   uint8_t x[kXBytes];
   float red[2][kWaves][256];
   float inv_rms[kMaxTok * kMaxReq];
+  Unit units[kSchCount][kMaxWgUnits];  // this workgroup's dense units, per schedule
+  int32_t nunits[kSchCount];
   int32_t flag;
 };
 
@@ -99,8 +101,57 @@ __device__ __forceinline__ void st_wt16(void* p, u32x4_t d) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(d) : "memory");
 }
 
+// Keeps the loads of consecutive ring slots in program order. Without it the
+// scheduler may reorder a prologue's independent slot loads, and the wait
+// counts at the loop head, which must hold for the first iteration too, then
+// drain the whole ring on every iteration.
+__device__ __forceinline__ void ring_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Waits for every outstanding vector memory operation (s_waitcnt vmcnt(0),
+// other counters untouched). Placed where all loads have completed anyway
+// (the end of an activation fill), it also clears the compiler's record of
+// pending loads, so the wait counts of a following ring loop are computed
+// from that loop alone.
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ctx[r] without a dynamic index into the kernel argument (which would be a
+// vector load from the argument segment inside a ring loop).
+__device__ __forceinline__ int ctx_of(const Params& p, int r) {
+  int c = __builtin_amdgcn_readfirstlane(p.ctx[0]);
+#pragma unroll
+  for (int i = 1; i < kMaxReq; ++i) c = (r == i) ? __builtin_amdgcn_readfirstlane(p.ctx[i]) : c;
+  return c;
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Pairwise tree sum over aligned groups of n lanes (n a power of two <= 64),
+// adjacent pairs first: level l adds the partner block of 2^(l-1) lanes.
+// After each level every lane of a block holds the same value, so any lane
+// permutation that maps a block onto its partner gives the same sums (fp32
+// addition is commutative): quad_perm [1,0,3,2] and [2,3,0,1], then the
+// half-row and row mirrors (DPP), then read-lanes of the 16-lane rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float lane_tree_sum(float acc, int n) {
+  if (n >= 2) acc = acc + dpp_f32<0xB1>(acc);   // quad_perm [1,0,3,2]
+  if (n >= 4) acc = acc + dpp_f32<0x4E>(acc);   // quad_perm [2,3,0,1]
+  if (n >= 8) acc = acc + dpp_f32<0x141>(acc);  // row_half_mirror
+  if (n >= 16) acc = acc + dpp_f32<0x140>(acc); // row_mirror
+  if (n >= 32) {
+    const float r0 = readlane_f32(acc, 0), r1 = readlane_f32(acc, 16);
+    const float r2 = readlane_f32(acc, 32), r3 = readlane_f32(acc, 48);
+    acc = (n == 32) ? (lane_id() < 32 ? r0 + r1 : r2 + r3) : (r0 + r1) + (r2 + r3);
+  }
+  return acc;
+}
+
 
 // ---------------------------------------------------------------------------
 // Grid barrier. All data exchanged between workgroups inside a launch is
@@ -204,34 +255,54 @@ __device__ __forceinline__ void compute_inv_rms(const Params& p, const float* h,
 
 // X = fp16(h * inv_rms * g), or fp16(h * g) when the caller applies inv_rms to
 // the projection's output instead (with_inv = false), or fp16(h) without the
-// norm; rounded to nearest even.
+// norm; rounded to nearest even. Item i = (token i / K8, elements 8*(i % K8)
+// .. +8); a thread's items share one k range (K8 divides the workgroup
+// size), and the loads of kFillBatch items are issued before any is used.
+constexpr int kFillBatch = 4;
+
 __device__ __forceinline__ void fill_x_norm(const Params& p, const float* h, const uint16_t* g, Smem& sm,
                                             bool with_inv = true) {
   const int K = p.H, NT = p.NT, K8 = K / 8;
-  for (int i = threadIdx.x; i < kMaxTok * K8; i += kThreads) {
-    int t = i / K8, k = (i % K8) * 8;
-    uint4 out = make_uint4(0, 0, 0, 0);
-    if (t < NT) {
-      const float4* hp = reinterpret_cast<const float4*>(h + (size_t)t * K + k);
-      float4 a = hp[0], b = hp[1];
-      float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      const float inv = with_inv ? sm.inv_rms[t] : 1.0f;
-      if (p.use_norm) {
-        uint4 gg = *reinterpret_cast<const uint4*>(g + k);
-        uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+  const int total = kMaxTok * K8;
+  const int k = (threadIdx.x % K8) * 8;
+  float gj[8];
+  {
+    const uint4 gg = *reinterpret_cast<const uint4*>(g + k);
+    const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float gj = bf2f((uint16_t)(gw[j >> 1] >> ((j & 1) * 16)));
-          v[j] = (v[j] * inv) * gj;
-        }
-      }
-      out.x = pack2(f2h(v[0]), f2h(v[1]));
-      out.y = pack2(f2h(v[2]), f2h(v[3]));
-      out.z = pack2(f2h(v[4]), f2h(v[5]));
-      out.w = pack2(f2h(v[6]), f2h(v[7]));
-    }
-    *reinterpret_cast<uint4*>(sm.x + t * x_stride(K) + k * 2) = out;
+    for (int j = 0; j < 8; ++j) gj[j] = p.use_norm ? bf2f((uint16_t)(gw[j >> 1] >> ((j & 1) * 16))) : 1.0f;
   }
+  for (int i0 = threadIdx.x; i0 < total; i0 += kFillBatch * kThreads) {
+    float4 a[kFillBatch], b[kFillBatch];
+#pragma unroll
+    for (int q = 0; q < kFillBatch; ++q) {
+      const int t = min((i0 + q * kThreads) / K8, NT - 1);
+      const float4* hp = reinterpret_cast<const float4*>(h + (size_t)t * K + k);
+      a[q] = hp[0];
+      b[q] = hp[1];
+    }
+#pragma unroll
+    for (int q = 0; q < kFillBatch; ++q) {
+      const int i = i0 + q * kThreads;
+      if (i >= total) break;
+      const int t = i / K8;
+      uint4 out = make_uint4(0, 0, 0, 0);
+      if (t < NT) {
+        float v[8] = {a[q].x, a[q].y, a[q].z, a[q].w, b[q].x, b[q].y, b[q].z, b[q].w};
+        const float inv = with_inv ? sm.inv_rms[t] : 1.0f;
+        if (p.use_norm) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = (v[j] * inv) * gj[j];
+        }
+        out.x = pack2(f2h(v[0]), f2h(v[1]));
+        out.y = pack2(f2h(v[2]), f2h(v[3]));
+        out.z = pack2(f2h(v[4]), f2h(v[5]));
+        out.w = pack2(f2h(v[6]), f2h(v[7]));
+      }
+      *reinterpret_cast<uint4*>(sm.x + t * x_stride(K) + k * 2) = out;
+    }
+  }
+  vm_drain();
   __syncthreads();
 }
 
@@ -272,35 +343,88 @@ __device__ __forceinline__ void fill_x_qkv(const Params& p, const float* h, cons
 
 // X = copy of a 16-bit activation matrix src [NT][K] (already fp16).
 __device__ __forceinline__ void fill_x_copy(const uint16_t* src, int K, int NT, Smem& sm) {
-  const int K8 = K / 8;
-  for (int i = threadIdx.x; i < kMaxTok * K8; i += kThreads) {
-    int t = i / K8, k = (i % K8) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (t < NT) v = *reinterpret_cast<const uint4*>(src + (size_t)t * K + k);
-    *reinterpret_cast<uint4*>(sm.x + t * x_stride(K) + k * 2) = v;
+  constexpr int B = 2 * kFillBatch;
+  const int K8 = K / 8, total = kMaxTok * K8;
+  for (int i0 = threadIdx.x; i0 < total; i0 += B * kThreads) {
+    uint4 v[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const int i = i0 + q * kThreads;
+      const int t = min(i / K8, NT - 1), k = (i % K8) * 8;
+      v[q] = *reinterpret_cast<const uint4*>(src + (size_t)t * K + k);
+    }
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const int i = i0 + q * kThreads;
+      if (i >= total) break;
+      const int t = i / K8, k = (i % K8) * 8;
+      *reinterpret_cast<uint4*>(sm.x + t * x_stride(K) + k * 2) = t < NT ? v[q] : make_uint4(0, 0, 0, 0);
+    }
   }
+  vm_drain();
   __syncthreads();
 }
 
-// X = sum over n partial slots of fp32 [n][NT][K], rounded to fp16.
+// X = sum over n partial slots of fp32 [n][NT][K] (slot order), rounded to fp16.
 __device__ __forceinline__ void fill_x_sum(const float* parts, int n, int K, int NT, Smem& sm) {
-  const int K8 = K / 8;
-  for (int i = threadIdx.x; i < kMaxTok * K8; i += kThreads) {
-    int t = i / K8, k = (i % K8) * 8;
-    uint4 out = make_uint4(0, 0, 0, 0);
-    if (t < NT) {
-      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int s = 0; s < n; ++s) {
-        const float4* q = reinterpret_cast<const float4*>(parts + ((size_t)s * NT + t) * K + k);
-        float4 a = q[0], b = q[1];
-        v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-        v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
-      }
-      out.x = pack2(f2h(v[0]), f2h(v[1])); out.y = pack2(f2h(v[2]), f2h(v[3]));
-      out.z = pack2(f2h(v[4]), f2h(v[5])); out.w = pack2(f2h(v[6]), f2h(v[7]));
+  const int K8 = K / 8, total = kMaxTok * K8;
+  for (int i0 = threadIdx.x; i0 < total; i0 += kFillBatch * kThreads) {
+    float v[kFillBatch][8];
+#pragma unroll
+    for (int q = 0; q < kFillBatch; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[q][j] = 0.0f;
+    int s = 0;
+    for (; s + 2 <= n; s += 2) {
+      float4 a[2][kFillBatch], b[2][kFillBatch];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < kFillBatch; ++q) {
+          const int i = i0 + q * kThreads;
+          const int t = min(i / K8, NT - 1), k = (i % K8) * 8;
+          const float4* src = reinterpret_cast<const float4*>(parts + ((size_t)(s + u) * NT + t) * K + k);
+          a[u][q] = src[0];
+          b[u][q] = src[1];
+        }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < kFillBatch; ++q) {
+          v[q][0] += a[u][q].x; v[q][1] += a[u][q].y; v[q][2] += a[u][q].z; v[q][3] += a[u][q].w;
+          v[q][4] += b[u][q].x; v[q][5] += b[u][q].y; v[q][6] += b[u][q].z; v[q][7] += b[u][q].w;
+        }
     }
-    *reinterpret_cast<uint4*>(sm.x + t * x_stride(K) + k * 2) = out;
+    if (s < n) {
+      float4 a[kFillBatch], b[kFillBatch];
+#pragma unroll
+      for (int q = 0; q < kFillBatch; ++q) {
+        const int i = i0 + q * kThreads;
+        const int t = min(i / K8, NT - 1), k = (i % K8) * 8;
+        const float4* src = reinterpret_cast<const float4*>(parts + ((size_t)s * NT + t) * K + k);
+        a[q] = src[0];
+        b[q] = src[1];
+      }
+#pragma unroll
+      for (int q = 0; q < kFillBatch; ++q) {
+        v[q][0] += a[q].x; v[q][1] += a[q].y; v[q][2] += a[q].z; v[q][3] += a[q].w;
+        v[q][4] += b[q].x; v[q][5] += b[q].y; v[q][6] += b[q].z; v[q][7] += b[q].w;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kFillBatch; ++q) {
+      const int i = i0 + q * kThreads;
+      if (i >= total) break;
+      const int t = i / K8, k = (i % K8) * 8;
+      uint4 out = make_uint4(0, 0, 0, 0);
+      if (t < NT) {
+        out.x = pack2(f2h(v[q][0]), f2h(v[q][1])); out.y = pack2(f2h(v[q][2]), f2h(v[q][3]));
+        out.z = pack2(f2h(v[q][4]), f2h(v[q][5])); out.w = pack2(f2h(v[q][6]), f2h(v[q][7]));
+      }
+      *reinterpret_cast<uint4*>(sm.x + t * x_stride(K) + k * 2) = out;
+    }
   }
+  vm_drain();
   __syncthreads();
 }
 
@@ -409,7 +533,7 @@ __device__ __forceinline__ void dense_epilogue(const Params& p, const EpiArgs& e
         if (is_v) c -= Dkv;
         int g = c / p.d, cc = c % p.d;
         int r = tok / p.T, t = tok % p.T;
-        size_t dst = (((size_t)r * p.nkv + g) * p.cap + p.ctx[r] + t) * p.d + cc;
+        size_t dst = (((size_t)r * p.nkv + g) * p.cap + ctx_of(p, r) + t) * p.d + cc;
         if (is_v) {
           st_wt(&ea.v_cache[dst], f2bf(v));
           if (ea.dbg_v) ea.dbg_v[(size_t)tok * Dkv + c] = v;
@@ -433,44 +557,55 @@ __device__ __forceinline__ void dense_epilogue(const Params& p, const EpiArgs& e
   }
 }
 
-// Runs this workgroup's dense units; the first kRing units' weights are
-// already in flight in the ring (requested by dense_prefetch before the
-// preceding barrier wait).
+// A unit from this workgroup's LDS copy of a schedule, as wave-uniform values.
+__device__ __forceinline__ Unit lds_unit(const Smem& sm, int sch, int i) {
+  const Unit u = sm.units[sch][i];
+  return Unit{__builtin_amdgcn_readfirstlane(u.tile), __builtin_amdgcn_readfirstlane(u.k0),
+              __builtin_amdgcn_readfirstlane(u.klen), __builtin_amdgcn_readfirstlane(u.slot)};
+}
+
+// Runs this workgroup's dense units of schedule `sch`; the first kRing units'
+// weights are already in flight in the ring (requested by dense_prefetch
+// before the preceding barrier wait).
 template <Epi E>
-__device__ __forceinline__ void dense_phase(const Params& p, const Sched& sc, const uint16_t* W, int ldw, int K,
+__device__ __forceinline__ void dense_phase(const Params& p, int sch, const uint16_t* W, int ldw, int K,
                                             const EpiArgs& ea, Smem& sm, DenseSlot (&ring)[kRing]) {
   constexpr bool RES = E == Epi::OProj || E == Epi::Unpool;
-  const int b0 = sc.off[blockIdx.x], b1 = sc.off[blockIdx.x + 1];
-  if (b0 >= b1) return;
+  const int n = sm.nunits[sch];
+  if (n <= 0) return;
   int rb = 0;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int base = b0; base < b1; base += kRing) {
+  for (int base = 0; base < n; base += kRing) {
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       const int ui = base + i;
-      const Unit u = sc.units[min(ui, b1 - 1)];
+      const Unit u = lds_unit(sm, sch, min(ui, n - 1));
       if (u.slot & kUnitFirst) acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
       acc = dense_compute(sm, K, u, ring[i], acc);
-      if (ui < b1 && (u.slot & kUnitLast)) {
+      if (ui < n && (u.slot & kUnitLast)) {
         red_store(sm, rb, acc);
         __syncthreads();
         dense_epilogue<E>(p, ea, u, sm, rb, ring[i].res);
         rb ^= 1;
       }
-      dense_issue<RES>(sc.units[min(ui + kRing, b1 - 1)], W, ldw, ea.res, p.H, p.NT, ring[i]);
+      dense_issue<RES>(lds_unit(sm, sch, min(ui + kRing, n - 1)), W, ldw, ea.res, p.H, p.NT, ring[i]);
+      ring_fence();
     }
   }
   __syncthreads();
 }
 
 template <Epi E>
-__device__ __forceinline__ void dense_prefetch(const Params& p, const Sched& sc, const uint16_t* W, int ldw,
-                                               const float* res, DenseSlot (&ring)[kRing]) {
+__device__ __forceinline__ void dense_prefetch(const Params& p, int sch, const uint16_t* W, int ldw,
+                                               const float* res, const Smem& sm, DenseSlot (&ring)[kRing]) {
   constexpr bool RES = E == Epi::OProj || E == Epi::Unpool;
-  const int b0 = sc.off[blockIdx.x], b1 = sc.off[blockIdx.x + 1];
-  if (b0 >= b1) return;
+  const int n = sm.nunits[sch];
+  if (n <= 0) return;
 #pragma unroll
-  for (int i = 0; i < kRing; ++i) dense_issue<RES>(sc.units[min(b0 + i, b1 - 1)], W, ldw, res, p.H, p.NT, ring[i]);
+  for (int i = 0; i < kRing; ++i) {
+    dense_issue<RES>(lds_unit(sm, sch, min(i, n - 1)), W, ldw, res, p.H, p.NT, ring[i]);
+    ring_fence();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -485,16 +620,22 @@ struct AttnItem {
 };
 
 __device__ __forceinline__ void attn_range(const Params& p, const LayerW& lw, int r, int& lo, int& hi) {
-  const int ctx = p.ctx[r];
+  const int ctx = ctx_of(p, r);
   lo = (lw.window > 0) ? max(0, ctx - lw.window + 1) : 0;
   hi = ctx + p.T - 1;
 }
 
-__device__ __forceinline__ int attn_splits(const Params& p, int nkeys, int grid) {
-  int cap_s = min(64, grid / (p.R * p.nkv));  // the merge keeps one split per lane
+// Keys per split: a whole number of chunks, as few as the split cap allows
+// (one chunk per item where the grid has room).
+__device__ __forceinline__ int attn_split_keys(const Params& p, int nkeys, int grid) {
+  int cap_s = min(kMaxSplits, grid / (p.R * p.nkv));
   if (cap_s < 1) cap_s = 1;
-  int s = (nkeys + 255) / 256;
-  return s < 1 ? 1 : (s > cap_s ? cap_s : s);
+  const int per = kAttnChunk * cap_s;
+  return kAttnChunk * ((nkeys + per - 1) / per);
+}
+__device__ __forceinline__ int attn_splits(const Params& p, int nkeys, int grid) {
+  const int cs = attn_split_keys(p, nkeys, grid);
+  return (nkeys + cs - 1) / cs;
 }
 
 // Item of a flat index; returns false if idx is past the last item.
@@ -510,7 +651,7 @@ __device__ __forceinline__ bool attn_item(const Params& p, const LayerW& lw, int
       it.g = idx / S;
       it.s = idx % S;
       it.nsplit = S;
-      int cs = (nk + S - 1) / S;
+      const int cs = attn_split_keys(p, nk, grid);
       it.k_begin = lo + it.s * cs;
       it.k_end = min(hi + 1, it.k_begin + cs);
       return true;
@@ -552,7 +693,7 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
   const int Dq = p.nq * p.d;
   const bool active = w < group;
   const int h = it.g * group + w;
-  const int ctx = p.ctx[it.r];
+  const int ctx = ctx_of(p, it.r);
   const int window = lw.window;
   constexpr int KS = D / 32;     // MFMA steps over the head dim
   constexpr int DT = D / 16;     // d tiles of the PV product
@@ -562,25 +703,41 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
   uint16_t* Vt = Ks + kAttnChunk * RS;
 
   // Q^T operand: col = token r_, 8 consecutive dims per lane group, summed over slices.
+  // Q^T operand: all split-K slices of Q are requested at once (one round
+  // trip; lanes of inactive waves or tokens read an in-range row and are
+  // zeroed), then summed in slice order.
   uint4 qb[KS];
+  {
+    const int tok = it.r * p.T + min(r_, p.T - 1);
+    const int hq = active ? h : it.g * group;
+    float4 qa[kMaxQSlices][KS], qc[kMaxQSlices][KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qb[s] = make_uint4(0, 0, 0, 0);
-  if (active && r_ < p.T) {
-    const int tok = it.r * p.T + r_;
+    for (int sl = 0; sl < kMaxQSlices; ++sl) {
+      const int slc = min(sl, p.q_slices - 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const float4* q4 = reinterpret_cast<const float4*>(
+            p.qpart + ((size_t)slc * p.NT + tok) * Dq + hq * D + s * 32 + g_ * 8);
+        qa[sl][s] = q4[0];
+        qc[sl][s] = q4[1];
+      }
+    }
+    const bool use = active && r_ < p.T;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int sl = 0; sl < p.q_slices; ++sl) {
-        const float4* q4 = reinterpret_cast<const float4*>(
-            p.qpart + ((size_t)sl * p.NT + tok) * Dq + h * D + s * 32 + g_ * 8);
-        float4 a = q4[0], b = q4[1];
-        v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-        v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+#pragma unroll
+      for (int sl = 0; sl < kMaxQSlices; ++sl) {
+        if (sl < p.q_slices) {
+          const float4 a = qa[sl][s], b = qc[sl][s];
+          v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+          v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+        }
       }
-      qb[s].x = pack2(f2h(v[0]), f2h(v[1]));
-      qb[s].y = pack2(f2h(v[2]), f2h(v[3]));
-      qb[s].z = pack2(f2h(v[4]), f2h(v[5]));
-      qb[s].w = pack2(f2h(v[6]), f2h(v[7]));
+      qb[s].x = use ? pack2(f2h(v[0]), f2h(v[1])) : 0u;
+      qb[s].y = use ? pack2(f2h(v[2]), f2h(v[3])) : 0u;
+      qb[s].z = use ? pack2(f2h(v[4]), f2h(v[5])) : 0u;
+      qb[s].w = use ? pack2(f2h(v[6]), f2h(v[7])) : 0u;
     }
   }
 
@@ -600,8 +757,11 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
   // K pieces: consecutive threads walk a key's dims (coalesced rows);
   // V pieces: consecutive threads walk keys at fixed dims, so the transposed
   // LDS writes of a wave land on consecutive addresses.
-  uint4 kreg[PER], vreg[PER];
-  auto load_chunk = [&](int c) {
+  // Two chunks of K/V are in flight in registers while one is computed. The
+  // loads are unconditional: a chunk past the item's end re-reads its last
+  // row (in bounds; masked below), so the wait counts stay static.
+  uint4 kreg0[PER], vreg0[PER], kreg1[PER], vreg1[PER];
+  auto load_chunk = [&](int c, uint4 (&kr)[PER], uint4 (&vr)[PER]) {
     int kb = it.k_begin + c * kAttnChunk;
     static_assert(CH16 % kThreads == 0, "a chunk is a whole number of 16-byte pieces per thread");
 #pragma unroll
@@ -609,33 +769,46 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
       int i = threadIdx.x + j * kThreads;
       // keys past the item's end read its last row (finite values, masked later)
       const int key = i / (D / 8), c8 = (i % (D / 8)) * 8;
-      kreg[j] = *reinterpret_cast<const uint4*>(kc + (size_t)min(kb + key, it.k_end - 1) * D + c8);
+      kr[j] = *reinterpret_cast<const uint4*>(kc + (size_t)min(kb + key, it.k_end - 1) * D + c8);
       const int vkey = i % kAttnChunk, vc8 = (i / kAttnChunk) * 8;
-      vreg[j] = *reinterpret_cast<const uint4*>(vc + (size_t)min(kb + vkey, it.k_end - 1) * D + vc8);
+      vr[j] = *reinterpret_cast<const uint4*>(vc + (size_t)min(kb + vkey, it.k_end - 1) * D + vc8);
     }
   };
-  if (nchunks > 0) load_chunk(0);
-  for (int c = 0; c < nchunks; ++c) {
-    __syncthreads();
+  auto stage_chunk = [&](const uint4 (&kr)[PER], const uint4 (&vr)[PER]) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       int i = threadIdx.x + j * kThreads;
-      {
-        int key = i / (D / 8), c8 = (i % (D / 8)) * 8;
-        *reinterpret_cast<uint4*>(Ks + key * RS + c8) = bf8_to_h8(kreg[j]);
-        int vkey = i % kAttnChunk, vc8 = (i / kAttnChunk) * 8;
-        const uint4 vh = bf8_to_h8(vreg[j]);
-        const uint32_t vw[4] = {vh.x, vh.y, vh.z, vh.w};
+      int key = i / (D / 8), c8 = (i % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(Ks + key * RS + c8) = bf8_to_h8(kr[j]);
+      int vkey = i % kAttnChunk, vc8 = (i / kAttnChunk) * 8;
+      const uint4 vh = bf8_to_h8(vr[j]);
+      const uint32_t vw[4] = {vh.x, vh.y, vh.z, vh.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          Vt[(vc8 + 2 * q) * VS + vkey] = (uint16_t)(vw[q] & 0xFFFFu);
-          Vt[(vc8 + 2 * q + 1) * VS + vkey] = (uint16_t)(vw[q] >> 16);
-        }
+      for (int q = 0; q < 4; ++q) {
+        Vt[(vc8 + 2 * q) * VS + vkey] = (uint16_t)(vw[q] & 0xFFFFu);
+        Vt[(vc8 + 2 * q + 1) * VS + vkey] = (uint16_t)(vw[q] >> 16);
       }
     }
-    if (c + 1 < nchunks) load_chunk(c + 1);
+  };
+  load_chunk(0, kreg0, vreg0);
+  ring_fence();
+  load_chunk(1, kreg1, vreg1);
+  ring_fence();
+  for (int c0 = 0; c0 < nchunks; c0 += 2) {
+#pragma unroll
+   for (int half = 0; half < 2; ++half) {
+    const int c = c0 + half;
     __syncthreads();
-    if (!active) continue;
+    if (half == 0) {
+      stage_chunk(kreg0, vreg0);
+      load_chunk(c + 2, kreg0, vreg0);
+    } else {
+      stage_chunk(kreg1, vreg1);
+      load_chunk(c + 2, kreg1, vreg1);
+    }
+    ring_fence();
+    __syncthreads();
+    if (!active || c >= nchunks) continue;
     const int kb = it.k_begin + c * kAttnChunk;
     // scores for 4 key tiles of 16
     float sc[4][4];
@@ -698,6 +871,7 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
         o[dt] = mfma_f16(av, bp, o[dt]);
       }
     }
+   }
   }
   if (active && r_ < p.T) {
     float* rec = apart_at(p, blockIdx.x, w, r_);
@@ -711,63 +885,53 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
   }
 }
 
-// Merge of the split partials (log-sum-exp in base 2): one wave per
-// (token, q head) row; lane s < S holds split s's (m, l), lanes split the dims.
+// Merge of the split partials (log-sum-exp in base 2). One wave per
+// (token, q head, 32 dims): lane l takes dim d0 + (l & 31) of the splits
+// s = (l >> 5) + 2i, and lane s < S also holds split s's (m, l). Every
+// partial is requested at once; the per-split factors 2^(m_s - M) reach the
+// lanes by read-lane, and the two half-waves' sums meet in one exchange.
 template <bool debug>
 __device__ __forceinline__ void merge_phase(const Params& p, const LayerW& lw) {
   const int D = p.d, Dq = p.nq * D, group = p.nq / p.nkv;
-  const int lane = lane_id();
-  const int rows = p.NT * p.nq;
+  const int lane = lane_id(), half = lane >> 5;
+  const int qpr = D / 32;
+  const int tasks = p.NT * p.nq * qpr;
   const int nw = gridDim.x * kWaves;
-  for (int row = blockIdx.x * kWaves + wave_id(); row < rows; row += nw) {
+  for (int task = blockIdx.x * kWaves + wave_id(); task < tasks; task += nw) {
+    const int row = task / qpr, dq = task - row * qpr;
     const int h = row % p.nq, tok = row / p.nq;
     const int r = tok / p.T, t = tok % p.T;
     const int g = h / group, w = h % group;
     int S;
     const int base = attn_item_base(p, lw, r, g, gridDim.x, S);
-    float m = -INFINITY, l = 0.0f;
-    if (lane < S) {
-      const float* rec = apart_at(p, base + lane, w, t);
-      m = rec[D];
-      l = rec[D + 1];
+    const int dim = dq * 32 + (lane & 31);
+    const int nper = (S + 1) / 2;  // splits per half-wave (the odd half may have one fewer)
+    float ov[kMaxSplits / 2];
+#pragma unroll
+    for (int i = 0; i < kMaxSplits / 2; ++i) {
+      if (i < nper) ov[i] = apart_at(p, base + min(half + 2 * i, S - 1), w, t)[dim];
     }
-    float M = m;
+    float2 ml = make_float2(-INFINITY, 0.0f);
+    if (lane < S) ml = *reinterpret_cast<const float2*>(apart_at(p, base + lane, w, t) + D);
+    float M = ml.x;
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-    float L = l * f;
+    const float f = (ml.x == -INFINITY) ? 0.0f : exp2f(ml.x - M);
+    float L = ml.y * f;
     for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-    const int c = 2 * lane;
-    float O0 = 0.0f, O1 = 0.0f;
-    int s = 0;
-    for (; s + 16 <= S; s += 16) {
-      float2 ov[16];
-      float fv[16];
+    float O = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        ov[j] = c < D ? *reinterpret_cast<const float2*>(apart_at(p, base + s + j, w, t) + c) : make_float2(0.f, 0.f);
-        fv[j] = __shfl(f, s + j);
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        O0 = fmaf(ov[j].x, fv[j], O0);
-        O1 = fmaf(ov[j].y, fv[j], O1);
+    for (int i = 0; i < kMaxSplits / 2; ++i) {
+      if (i < nper) {
+        const float fe = readlane_f32(f, 2 * i), fo = readlane_f32(f, min(2 * i + 1, kMaxSplits - 1));
+        const bool valid = half + 2 * i < S;
+        O = fmaf(ov[i], valid ? (half ? fo : fe) : 0.0f, O);
       }
     }
-    for (; s < S; ++s) {
-      const float fs = __shfl(f, s);
-      if (c < D) {
-        const float2 o2 = *reinterpret_cast<const float2*>(apart_at(p, base + s, w, t) + c);
-        O0 = fmaf(o2.x, fs, O0);
-        O1 = fmaf(o2.y, fs, O1);
-      }
-    }
-    if (c < D) {
-      const float out0 = O0 / L, out1 = O1 / L;
-      st_wt(reinterpret_cast<uint32_t*>(p.attn + (size_t)tok * Dq + h * D + c), pack2(f2h(out0), f2h(out1)));
-      if (debug) if (p.dbg.attn) {
-        p.dbg.attn[(size_t)tok * Dq + h * D + c] = out0;
-        p.dbg.attn[(size_t)tok * Dq + h * D + c + 1] = out1;
-      }
+    O += __shfl_xor(O, 32);
+    if (half == 0) {
+      const float out = O / L;
+      st_wt(p.attn + (size_t)tok * Dq + h * D + dim, f2h(out));
+      if (debug) if (p.dbg.attn) p.dbg.attn[(size_t)tok * Dq + h * D + dim] = out;
     }
   }
 }
@@ -807,13 +971,24 @@ __device__ __forceinline__ void fill_x_pool_router(const Params& p, Smem& sm) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) gv[j] = bf2f((uint16_t)(gw[j >> 1] >> ((j & 1) * 16)));
   }
-  for (int it = 0; it < nit; ++it) {
+  for (int it0 = 0; it0 < nit; it0 += kFillBatch) {
+   float4 ha[kFillBatch], hb[kFillBatch];
+#pragma unroll
+   for (int q = 0; q < kFillBatch; ++q) {
+     const int t = min(threadIdx.x / K8 + (it0 + q) * tstep, NT - 1);
+     const float4* hp = reinterpret_cast<const float4*>(p.h1 + (size_t)t * K + j8 * 8);
+     ha[q] = hp[0];
+     hb[q] = hp[1];
+   }
+#pragma unroll
+   for (int q = 0; q < kFillBatch; ++q) {
+    const int it = it0 + q;
+    if (it >= nit) break;
     const int t = threadIdx.x / K8 + it * tstep;
     uint4 out = make_uint4(0, 0, 0, 0);
     float acc = 0.0f;
     if (t < NT) {
-      const float4* hp = reinterpret_cast<const float4*>(p.h1 + (size_t)t * K + j8 * 8);
-      const float4 a = hp[0], b = hp[1];
+      const float4 a = ha[q], b = hb[q];
       float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
       const float inv = sm.inv_rms[t];
       if (p.use_norm) {
@@ -829,13 +1004,14 @@ __device__ __forceinline__ void fill_x_pool_router(const Params& p, Smem& sm) {
     }
     if (t < kMaxTok) *reinterpret_cast<uint4*>(sm.x + t * x_stride(K) + j8 * 16) = out;
     if (route) {
-      for (int o = 1; o < inwave; o <<= 1) acc = acc + __shfl_xor(acc, o);
+      acc = lane_tree_sum(acc, inwave);
       if (K8 <= 64) {
         if (j8 == 0 && t < NT) st_wt(&p.logits[(size_t)t * p.E + e], acc + bias);
       } else if (lane == 0 && t < kMaxTok) {
         blk[t * 8 + j8 / 64] = acc;
       }
     }
+   }
   }
   if (route && K8 > 64) {
     __syncthreads();
@@ -849,6 +1025,7 @@ __device__ __forceinline__ void fill_x_pool_router(const Params& p, Smem& sm) {
       st_wt(&p.logits[(size_t)threadIdx.x * p.E + e], r + bias);
     }
   }
+  vm_drain();
   __syncthreads();
 }
 
@@ -875,7 +1052,7 @@ struct Route {
   float ts_gu[kMaxTok * kMaxK];             // per selected slot: tensor scale of gate_up
   float ts_dn[kMaxTok * kMaxK];             // ... and of down
   int32_t count[kMaxE];                     // selections per expert (routing histogram)
-  uint32_t mask[kMaxE / 32];
+  int32_t pos[kMaxE];                       // slot of a selected expert in sel, else -1
 };
 
 constexpr int kRouteOff = kMaxTok * (2048 * 2 + 16);  // after the pooled X (P <= 2048)
@@ -883,89 +1060,151 @@ static_assert(kRouteOff + (int)sizeof(Route) <= kXBytes, "route tables must fit 
 
 __device__ __forceinline__ Route& route_of(Smem& sm) { return *reinterpret_cast<Route*>(sm.x + kRouteOff); }
 
-// Top-k by (logit descending, index ascending); gates = softmax of the selected logits.
+// GEMM1's staging of SwiGLU outputs follows the route tables.
+constexpr int kG1StageOff = (kRouteOff + (int)sizeof(Route) + 255) / 256 * 256;
+
+// Order-preserving map of a finite fp32 value to uint32 (larger float =>
+// larger key); key 0 is below every finite value.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v == 0.0f ? 0.0f : v);  // -0 ties with +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int popc64(uint64_t m) { return __builtin_popcountll(m); }
+
+// Top-k by (logit descending, index ascending); gates = softmax of the
+// selected logits. One wave per token: the k-th largest key is found by a
+// radix select over the 32 key bits (a ballot and popcount per bit), the
+// selected set is every key above it plus the lowest-index ties, and the
+// selected entries are ranked in LDS. The routing tables are then built
+// without serial loops.
 __device__ __forceinline__ void routing(const Params& p, Smem& sm, bool write_out) {
   Route& rt = route_of(sm);
   const int lane = lane_id(), w = wave_id();
-  const int E = p.E, K = p.topk;
-  if (threadIdx.x < kMaxE / 32) rt.mask[threadIdx.x] = 0;
-  if (threadIdx.x < kMaxE) rt.count[threadIdx.x] = 0;
-  __syncthreads();
-  for (int t = w; t < p.NT; t += kWaves) {
-    const float* lg = p.logits + (size_t)t * E;
-    float v[kMaxE / 64];
-    int taken = 0;
+  const int E = p.E, K = p.topk, NT = p.NT;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (threadIdx.x < kMaxE) {
+    rt.count[threadIdx.x] = 0;
+    rt.pos[threadIdx.x] = -1;
+  }
+  // both tokens' logits first (one round trip)
+  constexpr int TPW = kMaxTok / kWaves;  // tokens per wave
+  float v[TPW][kMaxE / 64];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int t = min(w + tt * kWaves, NT - 1);
 #pragma unroll
     for (int j = 0; j < kMaxE / 64; ++j) {
-      int e = lane + j * 64;
-      v[j] = e < E ? lg[e] : -INFINITY;
-      if (e >= E) taken |= 1 << j;
+      const int e = lane + j * 64;
+      v[tt][j] = p.logits[(size_t)t * E + min(e, E - 1)];
     }
-    float sel_v[kMaxK];
-    for (int r = 0; r < K; ++r) {
-      // lane best: largest value, lowest index among not taken
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+  }
+  __syncthreads();
 #pragma unroll
-      for (int j = 0; j < kMaxE / 64; ++j) {
-        int e = lane + j * 64;
-        if (!(taken & (1 << j)) && (v[j] > bv || (v[j] == bv && e < bi))) { bv = v[j]; bi = e; }
-      }
-      for (int o = 32; o >= 1; o >>= 1) {
-        float ov = __shfl_xor(bv, o);
-        int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if ((bi & 63) == lane) taken |= 1 << (bi >> 6);
-      sel_v[r] = bv;
-      if (lane == 0) rt.ids[t][r] = bi;
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int t = w + tt * kWaves;
+    if (t >= NT) break;
+    uint32_t key[kMaxE / 64];
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) key[j] = (lane + j * 64 < E) ? order_key(v[tt][j]) : 0u;
+    uint32_t T = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = T | (1u << b);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxE / 64; ++j) cnt += popc64(__ballot(key[j] >= cand));
+      if (cnt >= K) T = cand;
     }
-    if (lane == 0) {
-      float m = sel_v[0];
-      for (int r = 1; r < K; ++r) m = fmaxf(m, sel_v[r]);
-      float ex[kMaxK], s = 0.0f;
-      for (int r = 0; r < K; ++r) { ex[r] = expf(sel_v[r] - m); s += ex[r]; }
-      for (int r = 0; r < K; ++r) rt.gates[t][r] = ex[r] / s;
+    int n_gt = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) n_gt += popc64(__ballot(key[j] > T));
+    int ties_before = 0;  // ties with a lower index (index = lane + 64*j)
+    bool sel[kMaxE / 64];
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) {
+      const uint64_t tie = __ballot(key[j] == T);
+      const int my_rank = ties_before + popc64(tie & lt_mask);
+      sel[j] = key[j] > T || (key[j] == T && my_rank < K - n_gt);
+      ties_before += popc64(tie);
     }
+    // compact the k selected (index order) into per-wave LDS scratch
+    float* scr = &sm.red[0][w][0];  // [k] value, [k] index, as floats/bits
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) {
+      const uint64_t m = __ballot(sel[j]);
+      if (sel[j]) {
+        const int q = base + popc64(m & lt_mask);
+        scr[q] = v[tt][j];
+        scr[kMaxK + q] = __builtin_bit_cast(float, lane + j * 64);
+      }
+      base += popc64(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < K) {
+      const float mv = scr[lane];
+      const int me = __builtin_bit_cast(int, scr[kMaxK + lane]);
+      const uint32_t mk = order_key(mv);
+      int rank = 0;
+      float mx = mv;
+      for (int q = 0; q < K; ++q) {
+        const float ov = scr[q];
+        const int oe = __builtin_bit_cast(int, scr[kMaxK + q]);
+        const uint32_t ok = order_key(ov);
+        rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
+        mx = fmaxf(mx, ov);
+      }
+      rt.ids[t][rank] = me;
+      scr[2 * kMaxK + rank] = expf(mv - mx);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < K) {
+      float ssum = 0.0f;
+      for (int q = 0; q < K; ++q) ssum += scr[2 * kMaxK + q];  // rank order
+      rt.gates[t][lane] = scr[2 * kMaxK + lane] / ssum;
+    }
+    __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
-  // selected set
-  if (threadIdx.x < p.NT * K) {
-    int t = threadIdx.x / K, r = threadIdx.x % K;
-    int e = rt.ids[t][r];
-    atomicOr(&rt.mask[e >> 5], 1u << (e & 31));
-    atomicAdd(&rt.count[e], 1);
+  // histogram and membership
+  if (threadIdx.x < NT * K) {
+    const int t = threadIdx.x / K, r = threadIdx.x % K;
+    atomicAdd(&rt.count[rt.ids[t][r]], 1);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int q = 0; q < kMaxE / 32; ++q) {
-      uint32_t m = rt.mask[q];
-      while (m) {
-        int b = __builtin_ctz(m);
-        m &= m - 1;
-        rt.sel[n++] = q * 32 + b;
+  // selected set in ascending expert order: wave 0 ranks the experts with a
+  // nonzero count (lane l holds experts l, l+64, l+128, l+192)
+  if (w == 0) {
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) {
+      const int e = lane + j * 64;
+      const bool used = e < E && rt.count[e] > 0;
+      const uint64_t m = __ballot(used);
+      if (used) {
+        const int q = base + popc64(m & lt_mask);
+        rt.sel[q] = e;
+        rt.pos[e] = q;
       }
+      base += popc64(m);
     }
-    rt.n_sel = n;
+    if (lane == 0) rt.n_sel = base;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < rt.n_sel * kMaxTok; i += kThreads) {
-    int j = i / kMaxTok, t = i % kMaxTok;
-    float gv = 0.0f;
-    if (t < p.NT)
-      for (int r = 0; r < K; ++r)
-        if (rt.ids[t][r] == rt.sel[j]) gv = rt.gates[t][r];
-    rt.tokgate[j][t] = gv;
-  }
-  for (int j = threadIdx.x; j < rt.n_sel; j += kThreads) {
+  const int n_sel = rt.n_sel;
+  for (int i = threadIdx.x; i < n_sel * kMaxTok; i += kThreads) (&rt.tokgate[0][0])[i] = 0.0f;
+  for (int j = threadIdx.x; j < n_sel; j += kThreads) {
     rt.ts_gu[j] = p.cur.e_ts[2 * rt.sel[j]];
     rt.ts_dn[j] = p.cur.e_ts[2 * rt.sel[j] + 1];
   }
-  if (write_out && threadIdx.x < p.NT * K) {
-    int t = threadIdx.x / K, r = threadIdx.x % K;
-    if (p.out_ids) p.out_ids[t * K + r] = rt.ids[t][r];
-    if (p.out_gates) p.out_gates[t * K + r] = rt.gates[t][r];
+  __syncthreads();
+  if (threadIdx.x < NT * K) {
+    const int t = threadIdx.x / K, r = threadIdx.x % K;
+    rt.tokgate[rt.pos[rt.ids[t][r]]][t] = rt.gates[t][r];
+    if (write_out) {
+      if (p.out_ids) p.out_ids[t * K + r] = rt.ids[t][r];
+      if (p.out_gates) p.out_gates[t * K + r] = rt.gates[t][r];
+    }
   }
   if (write_out && p.hist && threadIdx.x < E) p.hist[(size_t)p.layer * E + threadIdx.x] = rt.count[threadIdx.x];
   __syncthreads();
@@ -996,106 +1235,119 @@ __device__ __forceinline__ void fp4_decode(uint4 codes, uint32_t sc2, uint4 out[
 }
 
 // GEMM1: gate/up projection of the selected experts with SwiGLU.
-// Unit = (selected slot j, i-tile it): rows gate[it*8 .. +8) and up[I + it*8 .. +8)
-// as the 16 MFMA columns; k = P split over the waves in steps of 128
-// (lane group g holds the 32 elements at step*128 + g*32; wave w owns steps
-// w and w + 8). Steps beyond P load a clamped address and read the zero A
-// operand, so every unit issues the same loads (see the dense engine).
-constexpr int kG1Ring = 4;  // GEMM1 units whose loads are in flight per wave
+// Unit = (selected slot j, i-tile it): gate rows it*8 .. +8 and up rows
+// I + it*8 .. +8 as the 16 MFMA columns, contracted over the whole pooled
+// dim P by one wave in P/128 steps (lane group g holds the 32 elements at
+// step*128 + g*32 of its row, the A operand the same k of the 16 tokens).
+// A workgroup owns a contiguous range of units and wave w takes every 8th
+// unit of it, so no partial sums cross waves. Each wave's loads run
+// kG1Ring steps ahead over its flat (unit, step) sequence, across unit
+// boundaries; the SwiGLU outputs are staged in LDS and written out once at
+// the end of the phase, so the loop issues nothing but loads and MFMA.
+constexpr int kG1Ring = 8;  // steps of loads in flight per wave
+static_assert(kG1StageOff + kG1StageBytes <= kXBytes, "GEMM1 staging must fit the X region");
 
-struct G1Slot {
-  uint4 c[2];
-  uint32_t s[2];
+struct G1Step {
+  uint4 c;     // 32 E2M1 codes of the lane's row
+  uint32_t s;  // their two E4M3 block scales (low 16 bits)
 };
 
-__device__ __forceinline__ void g1_issue(const Params& p, const Route& rt, int u, G1Slot& b) {
-  const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4, w = wave_id();
+// Wave-uniform unit/step cursor over the wave's units u0 + w + 8*m.
+struct G1Cursor {
+  int m, st;
+};
+
+__device__ __forceinline__ void g1_issue(const Params& p, const Route& rt, int u, int st, G1Step& b) {
+  const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4;
   const int I = p.I, P = p.P, ntile = I / 8;
-  const int j = u / ntile, it = u % ntile;
+  const int j = u / ntile, it = u - j * ntile;
   const int e = rt.sel[j];
   const int row = r_ < 8 ? it * 8 + r_ : I + it * 8 + (r_ - 8);
-  const uint8_t* codes = p.cur.e_gu + (size_t)e * (2 * I) * (P / 2) + (size_t)row * (P / 2);
-  const uint8_t* scs = p.cur.e_gu_sc + (size_t)e * (2 * I) * (P / 16) + (size_t)row * (P / 16);
-  const int nsteps = P / 128;
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int st = w + c * kWaves;
-    const int k = (st < nsteps ? st : 0) * 128 + g_ * 32;
-    b.c[c] = *reinterpret_cast<const uint4*>(codes + k / 2);
-    b.s[c] = *reinterpret_cast<const uint16_t*>(scs + k / 16);
-  }
-}
-
-template <bool debug>
-__device__ __forceinline__ void g1_unit(const Params& p, Smem& sm, const Route& rt, int u, bool valid,
-                                        const G1Slot& cur, int rb) {
-  const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4, w = wave_id();
-  const int I = p.I, P = p.P, ntile = I / 8;
-  const int nsteps = P / 128;
-  const int j = u / ntile, it = u % ntile;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int st = w + c * kWaves;
-    const bool kv = st < nsteps;
-    uint4 bw[4];
-    fp4_decode(cur.c[c], cur.s[c], bw);
-    const int kbase = st * 128 + g_ * 32;
-    const uint8_t* abase = kv ? sm.x + r_ * x_stride(P) + kbase * 2 : reinterpret_cast<const uint8_t*>(&sm.zero);
-    const int astep = kv ? 16 : 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc = mfma_f16(*reinterpret_cast<const uint4*>(abase + q * astep), bw[q], acc);
-    if constexpr (debug) {
-      const int e = rt.sel[j];
-      if (valid && kv && p.dbg.dq_gu && e == p.dbg.dq_expert) {
-        const int row = r_ < 8 ? it * 8 + r_ : I + it * 8 + (r_ - 8);
-        uint4* dst = reinterpret_cast<uint4*>(p.dbg.dq_gu + (size_t)row * P + kbase);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = bw[q];
-      }
-    }
-  }
-  if (!valid) return;
-  red_store(sm, rb, acc);
-  __syncthreads();
-  if (threadIdx.x < kMaxTok * 4) {
-    const int tok = threadIdx.x >> 2, c = (threadIdx.x & 3) * 2;
-    if (tok < p.NT) {
-      const float ts = rt.ts_gu[j], tg = rt.tokgate[j][tok];
-      uint16_t out[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        float gate = red_sum(sm, rb, tok * 16 + c + q) * ts;
-        float up = red_sum(sm, rb, tok * 16 + 8 + c + q) * ts;
-        float a = gate / (1.0f + expf(-gate)) * up;
-        out[q] = f2h(a * tg);
-      }
-      st_wt(reinterpret_cast<uint32_t*>(p.abuf + ((size_t)j * p.NT + tok) * I + it * 8 + c), pack2(out[0], out[1]));
-    }
-  }
+  const int k = st * 128 + g_ * 32;
+  const size_t r_all = (size_t)e * (2 * I) + row;
+  b.c = *reinterpret_cast<const uint4*>(p.cur.e_gu + r_all * (P / 2) + k / 2);
+  b.s = *reinterpret_cast<const uint16_t*>(p.cur.e_gu_sc + r_all * (P / 16) + k / 16);
 }
 
 template <bool debug>
 __device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
   Route& rt = route_of(sm);
-  const int ntile = p.I / 8;
+  uint8_t* stage = sm.x + kG1StageOff;
+  const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int I = p.I, P = p.P, ntile = I / 8, nsteps = P / 128;
   const int U = rt.n_sel * ntile;
   const int u0 = (int)((long long)blockIdx.x * U / gridDim.x);
   const int u1 = (int)((long long)(blockIdx.x + 1) * U / gridDim.x);
-  if (u0 >= u1) return;
-  G1Slot ring[kG1Ring];
-#pragma unroll
-  for (int i = 0; i < kG1Ring; ++i) g1_issue(p, rt, min(u0 + i, u1 - 1), ring[i]);
-  int rb = 0;
-  for (int base = u0; base < u1; base += kG1Ring) {
+  const int my_units = (u1 - u0 - w + kWaves - 1) / kWaves;  // units u0 + w + 8*m < u1
+  const int total = my_units > 0 ? my_units * nsteps : 0;
+  if (total > 0) {
+    G1Step ring[kG1Ring];
+    G1Cursor is{0, 0};  // next step to issue
+    auto issue_next = [&](G1Step& slot) {
+      const bool in = is.m < my_units;
+      const int m = in ? is.m : my_units - 1, st = in ? is.st : nsteps - 1;
+      g1_issue(p, rt, u0 + w + kWaves * m, st, slot);
+      if (++is.st == nsteps) { is.st = 0; ++is.m; }
+    };
 #pragma unroll
     for (int i = 0; i < kG1Ring; ++i) {
-      const int uu = base + i;
-      const bool valid = uu < u1;
-      g1_unit<debug>(p, sm, rt, min(uu, u1 - 1), valid, ring[i], rb);
-      if (valid) rb ^= 1;
-      g1_issue(p, rt, min(uu + kG1Ring, u1 - 1), ring[i]);
+      issue_next(ring[i]);
+      ring_fence();
     }
+    G1Cursor cs{0, 0};  // next step to compute
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int base = 0; base < total; base += kG1Ring) {
+#pragma unroll
+      for (int i = 0; i < kG1Ring; ++i) {
+        if (base + i < total) {
+          const int st = cs.st;
+          uint4 bw[4];
+          fp4_decode(ring[i].c, ring[i].s, bw);
+          const uint8_t* abase = sm.x + r_ * x_stride(P) + (st * 128 + g_ * 32) * 2;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc = mfma_f16(*reinterpret_cast<const uint4*>(abase + q * 16), bw[q], acc);
+          const int u = u0 + w + kWaves * cs.m;
+          const int j = u / ntile, it = u - j * ntile;
+          if constexpr (debug) {
+            if (p.dbg.dq_gu && rt.sel[j] == p.dbg.dq_expert) {
+              const int row = r_ < 8 ? it * 8 + r_ : I + it * 8 + (r_ - 8);
+              uint4* dst = reinterpret_cast<uint4*>(p.dbg.dq_gu + (size_t)row * P + st * 128 + g_ * 32);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) dst[q] = bw[q];
+            }
+          }
+          if (st == nsteps - 1) {
+            // acc[i] = D[token 4g+i][column r]: gate (r < 8) or up (r >= 8) of i-row it*8 + (r & 7).
+            const float ts = rt.ts_gu[j];
+            uint16_t* srow = reinterpret_cast<uint16_t*>(stage + (size_t)(u - u0) * 256);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float up = __shfl_xor(acc[q], 8);
+              const int tok = 4 * g_ + q;
+              if (r_ < 8) {
+                const float gate = acc[q] * ts;
+                const float a = gate / (1.0f + expf(-gate)) * (up * ts);
+                srow[tok * 8 + r_] = f2h(a * rt.tokgate[j][tok]);
+              }
+            }
+            acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+          if (++cs.st == nsteps) { cs.st = 0; ++cs.m; }
+        }
+        issue_next(ring[i]);
+        ring_fence();
+      }
+    }
+  }
+  __syncthreads();
+  // flush: 16 B per (unit, token) to abuf[j][token][it*8 .. +8]
+  const int NT = p.NT;
+  for (int q = threadIdx.x; q < (u1 - u0) * NT; q += kThreads) {
+    const int ul = q / NT, tok = q - ul * NT;
+    const int u = u0 + ul, j = u / ntile, it = u - j * ntile;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (size_t)ul * 256 + tok * 16);
+    st_wt16(p.abuf + ((size_t)j * NT + tok) * I + it * 8, v);
   }
   __syncthreads();
 }
@@ -1146,7 +1398,10 @@ __device__ __forceinline__ void gemm2_phase(const Params& p, Smem& sm) {
   if (j0 < j1) {
     G2Slot ring[kG2Ring];
 #pragma unroll
-    for (int i = 0; i < kG2Ring; ++i) g2_issue(p, rt, min(j0 + i, j1 - 1), tile, ring[i]);
+    for (int i = 0; i < kG2Ring; ++i) {
+      g2_issue(p, rt, min(j0 + i, j1 - 1), tile, ring[i]);
+      ring_fence();
+    }
     for (int base = j0; base < j1; base += kG2Ring) {
 #pragma unroll
       for (int i = 0; i < kG2Ring; ++i) {
@@ -1170,6 +1425,7 @@ __device__ __forceinline__ void gemm2_phase(const Params& p, Smem& sm) {
           }
         }
         g2_issue(p, rt, min(jj + kG2Ring, j1 - 1), tile, ring[i]);
+        ring_fence();
       }
     }
   }
@@ -1189,9 +1445,9 @@ __device__ __forceinline__ void gemm2_phase(const Params& p, Smem& sm) {
 // Phase-boundary slots of the self-timing trace (one uint64 per slot, per
 // workgroup, per launch; 100 MHz real-time counter).
 enum TraceSlot {
-  kTrStart = 0, kTrQkvOwn, kTrQkvOwnBar, kTrAttn, kTrAttnBar, kTrMerge, kTrMergeBar, kTrOproj,
-  kTrOprojBar, kTrRouterPool, kTrRouterPoolBar, kTrGemm1, kTrGemm1Bar, kTrGemm2, kTrGemm2Bar,
-  kTrUnpool, kTrUnpoolBar, kTrQkvNext, kTrSlots
+  kTrStart = 0, kTrQkvOwn, kTrQkvOwnBar, kTrAttn, kTrAttnBar, kTrMerge, kTrMergeBar, kTrOprojFill, kTrOproj,
+  kTrOprojBar, kTrPoolFill, kTrRouterPool, kTrRouterPoolBar, kTrRouting, kTrGemm1, kTrGemm1Bar, kTrGemm2,
+  kTrGemm2Bar, kTrUnpoolFill, kTrUnpool, kTrUnpoolBar, kTrQkvFill, kTrQkvNext, kTrSlots
 };
 static_assert(kTrSlots == kTraceSlots, "trace slot count");
 
@@ -1214,14 +1470,21 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   const int Nqkv = Dq + 2 * p.nkv * p.d;
   DenseSlot ring[kRing];
   if (threadIdx.x == 0) sm.zero = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int sch = 0; sch < kSchCount; ++sch) {
+    const int b0 = p.sched[sch].off[blockIdx.x], n = p.sched[sch].off[blockIdx.x + 1] - b0;
+    if (threadIdx.x < n) sm.units[sch][threadIdx.x] = p.sched[sch].units[b0 + threadIdx.x];
+    if (threadIdx.x == 0) sm.nunits[sch] = n;
+  }
+  __syncthreads();
 
   if constexpr ((MODE & kModeQkvOwn) != 0) {
-    dense_prefetch<Epi::Qkv>(p, p.s_qkv_own, p.cur.w_qkv, p.H, nullptr, ring);
+    dense_prefetch<Epi::Qkv>(p, kSchQkv, p.cur.w_qkv, p.H, nullptr, sm, ring);
     compute_inv_rms(p, p.h_in, nullptr, sm);
     fill_x_norm(p, p.h_in, p.cur.g_attn, sm, false);
     EpiArgs ea{p.cur.k_cache, p.cur.v_cache, nullptr, p.qpart, nullptr, DEBUG ? p.dbg.k_new : nullptr,
                DEBUG ? p.dbg.v_new : nullptr};
-    dense_phase<Epi::Qkv>(p, p.s_qkv_own, p.cur.w_qkv, p.H, p.H, ea, sm, ring);
+    dense_phase<Epi::Qkv>(p, kSchQkv, p.cur.w_qkv, p.H, p.H, ea, sm, ring);
     mark(kTrQkvOwn);
     bar_arrive(bar);
     if (!bar_wait(bar, sm)) return;
@@ -1247,19 +1510,20 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   merge_phase<DEBUG>(p, p.cur);
   mark(kTrMerge);
   bar_arrive(bar);
-  dense_prefetch<Epi::OProj>(p, p.s_oproj, p.cur.w_o, Dq, p.h_in, ring);
+  dense_prefetch<Epi::OProj>(p, kSchOproj, p.cur.w_o, Dq, p.h_in, sm, ring);
   if (!bar_wait(bar, sm)) return;
   mark(kTrMergeBar);
 
   // output projection + residual
   {
     fill_x_copy(p.attn, Dq, p.NT, sm);
+    mark(kTrOprojFill);
     EpiArgs ea{nullptr, nullptr, p.h_in, p.h1, p.ssq1, nullptr, nullptr};
-    dense_phase<Epi::OProj>(p, p.s_oproj, p.cur.w_o, Dq, Dq, ea, sm, ring);
+    dense_phase<Epi::OProj>(p, kSchOproj, p.cur.w_o, Dq, Dq, ea, sm, ring);
   }
   mark(kTrOproj);
   bar_arrive(bar);
-  dense_prefetch<Epi::Pool>(p, p.s_pool, p.cur.w_pool, p.H, nullptr, ring);
+  dense_prefetch<Epi::Pool>(p, kSchPool, p.cur.w_pool, p.H, nullptr, sm, ring);
   if (!bar_wait(bar, sm)) return;
   mark(kTrOprojBar);
   if (DEBUG && p.dbg.h1) {
@@ -1270,9 +1534,10 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   {
     compute_inv_rms(p, p.h1, p.ssq1, sm);
     fill_x_pool_router(p, sm);
+    mark(kTrPoolFill);
     if (DEBUG && p.dbg.n2 && blockIdx.x == 0) dump_n2(p, sm);
     EpiArgs ea{nullptr, nullptr, nullptr, p.ppart, nullptr, nullptr, nullptr};
-    dense_phase<Epi::Pool>(p, p.s_pool, p.cur.w_pool, p.H, p.H, ea, sm, ring);
+    dense_phase<Epi::Pool>(p, kSchPool, p.cur.w_pool, p.H, p.H, ea, sm, ring);
   }
   mark(kTrRouterPool);
   bar_arrive(bar);
@@ -1282,6 +1547,7 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   // routing (every workgroup) + experts' gate/up
   fill_x_sum(p.ppart, p.p_slices, p.P, p.NT, sm);
   routing(p, sm, blockIdx.x == 0);
+  mark(kTrRouting);
   if (DEBUG && blockIdx.x == 0) {
     if (p.dbg.logits)
       for (int i = threadIdx.x; i < p.NT * p.E; i += kThreads) p.dbg.logits[i] = p.logits[i];
@@ -1301,7 +1567,7 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   gemm2_phase<DEBUG>(p, sm);
   mark(kTrGemm2);
   bar_arrive(bar);
-  dense_prefetch<Epi::Unpool>(p, p.s_unpool, p.cur.w_unpool, p.P, p.h1, ring);
+  dense_prefetch<Epi::Unpool>(p, kSchUnpool, p.cur.w_unpool, p.P, p.h1, sm, ring);
   if (!bar_wait(bar, sm)) return;
   mark(kTrGemm2Bar);
 
@@ -1309,8 +1575,9 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   {
     const int parts = max(1, (int)gridDim.x / (p.P / 16));
     fill_x_sum(p.accpart, parts, p.P, p.NT, sm);
+    mark(kTrUnpoolFill);
     EpiArgs ea{nullptr, nullptr, p.h1, p.h_out, p.ssq2, nullptr, nullptr};
-    dense_phase<Epi::Unpool>(p, p.s_unpool, p.cur.w_unpool, p.P, p.P, ea, sm, ring);
+    dense_phase<Epi::Unpool>(p, kSchUnpool, p.cur.w_unpool, p.P, p.P, ea, sm, ring);
     if (DEBUG && p.dbg.acc && blockIdx.x == 0) {
       for (int i = threadIdx.x; i < p.NT * p.P; i += kThreads) {
         float v = 0.0f;
@@ -1323,12 +1590,13 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   mark(kTrUnpool);
   if constexpr ((MODE & kModeQkvNext) != 0) {
     bar_arrive(bar);
-    dense_prefetch<Epi::Qkv>(p, p.s_qkv_next, p.nxt.w_qkv, p.H, nullptr, ring);
+    dense_prefetch<Epi::Qkv>(p, kSchQkv, p.nxt.w_qkv, p.H, nullptr, sm, ring);
     if (!bar_wait(bar, sm)) return;
     mark(kTrUnpoolBar);
     fill_x_qkv(p, p.h_out, p.nxt.g_attn, p.ssq2, sm);
+    mark(kTrQkvFill);
     EpiArgs ea{p.nxt.k_cache, p.nxt.v_cache, nullptr, p.qpart, nullptr, nullptr, nullptr};
-    dense_phase<Epi::Qkv>(p, p.s_qkv_next, p.nxt.w_qkv, p.H, p.H, ea, sm, ring);
+    dense_phase<Epi::Qkv>(p, kSchQkv, p.nxt.w_qkv, p.H, p.H, ea, sm, ring);
     mark(kTrQkvNext);
   }
 }

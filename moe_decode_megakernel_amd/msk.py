@@ -49,9 +49,9 @@ class msk_io(ctypes.Structure):
                 ("debug", ctypes.POINTER(msk_debug)), ("trace", vp)]
 
 
-TRACE_SLOTS = ["start", "qkv_own", "qkv_own_bar", "attn", "attn_bar", "merge", "merge_bar", "oproj",
-               "oproj_bar", "router_pool", "router_pool_bar", "gemm1", "gemm1_bar", "gemm2", "gemm2_bar",
-               "unpool", "unpool_bar", "qkv_next"]
+TRACE_SLOTS = ["start", "qkv_own", "qkv_own_bar", "attn", "attn_bar", "merge", "merge_bar", "oproj_fill",
+               "oproj", "oproj_bar", "pool_fill", "router_pool", "router_pool_bar", "routing", "gemm1",
+               "gemm1_bar", "gemm2", "gemm2_bar", "unpool_fill", "unpool", "unpool_bar", "qkv_fill", "qkv_next"]
 MAX_GRID = 256
 
 
