@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-layers", default="0,1,2,3,4,5,6,7", help="layers of the step the oracle times")
     ap.add_argument("--trace", action="store_true",
                     help="after timing, run one step with the self-timing kernel and print the phase breakdown")
+    ap.add_argument("--expert-prefetch", type=int, default=None,
+                    help="experts per layer to prefetch speculatively (default 14; 0 = off)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference kernel that "
                          "scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -113,7 +115,7 @@ def main():
     dev = "cuda"
     stream = torch.cuda.current_stream()
     t0 = time.time()
-    handle = msk.Handle(msk.make_config(w))
+    handle = msk.Handle(msk.make_config(w, expert_prefetch=args.expert_prefetch))
     layers = []
     for l in range(w.n_layers):
         t = synth.device_layer(w, l, dev, stream_ptr=stream.cuda_stream)

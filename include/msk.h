@@ -81,6 +81,15 @@ typedef struct {
   int32_t kv_capacity;   /* cache rows per (request, kv head) */
   float rms_eps;
   uint32_t flags;
+  int32_t expert_prefetch; /* 0 (off) .. min(32, n_experts): speculative expert prefetch.
+                              At the start of each layer launch, the workgroups without
+                              attention work rank the layer's experts by how often the
+                              previous call selected them (count descending, index
+                              ascending; LMSYS post, newruntime.com "What happened":
+                              likely experts of the previous step are prefetched) and
+                              read the first expert_prefetch of them (codes and scales)
+                              so that they sit in the memory-side cache when the expert
+                              phase runs. No effect on results. */
 } msk_config;
 
 typedef struct {
@@ -129,6 +138,10 @@ typedef struct {
   int32_t* expert_ids;    /* device, may be NULL: [L][R*T][k] (verify_layer: [R*T][k]) */
   float* gates;           /* device, may be NULL: same shape as expert_ids */
   const msk_debug* debug; /* HOST struct, may be NULL; honoured by msk_verify_layer */
+  int32_t* prefetch_ids;  /* device, may be NULL: [L][expert_prefetch] (verify_layer:
+                             [expert_prefetch]) the prefetch list each layer used, i.e.
+                             the ranking of the previous call's selections of that layer
+                             (all counts zero before the first call on a handle). */
   uint64_t* trace;        /* device, may be NULL: self-timing variant of the kernel.
                              [launch][256][MSK_TRACE_SLOTS] uint64 stamps of the GPU's
                              100 MHz real-time counter, written by lane 0 of each
@@ -138,9 +151,11 @@ typedef struct {
 
 /* Trace slots, in execution order ("_BAR" = after the grid barrier that
  * follows; "_FILL" = after the phase's activation tile is in LDS; ROUTING =
- * after top-k and the routing tables). */
+ * after top-k and the routing tables; ATTN_Q / ATTN_KV = attention's query
+ * operand ready / first key-value chunk in LDS). */
 enum {
-  MSK_TR_START = 0, MSK_TR_QKV_OWN, MSK_TR_QKV_OWN_BAR, MSK_TR_ATTN, MSK_TR_ATTN_BAR,
+  MSK_TR_START = 0, MSK_TR_QKV_OWN, MSK_TR_QKV_OWN_BAR, MSK_TR_ATTN_Q, MSK_TR_ATTN_KV, MSK_TR_ATTN,
+  MSK_TR_ATTN_BAR,
   MSK_TR_MERGE, MSK_TR_MERGE_BAR, MSK_TR_OPROJ_FILL, MSK_TR_OPROJ, MSK_TR_OPROJ_BAR,
   MSK_TR_POOL_FILL, MSK_TR_ROUTER_POOL, MSK_TR_ROUTER_POOL_BAR, MSK_TR_ROUTING, MSK_TR_GEMM1,
   MSK_TR_GEMM1_BAR, MSK_TR_GEMM2, MSK_TR_GEMM2_BAR, MSK_TR_UNPOOL_FILL, MSK_TR_UNPOOL,

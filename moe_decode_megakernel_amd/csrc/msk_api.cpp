@@ -108,7 +108,8 @@ struct msk_handle_s {
   std::vector<msk_layer_desc> layers;
   std::vector<bool> loaded;
   int q_slices = 1, p_slices = 1;
-  msk::Sched sched[msk::kSchCount]{};
+  const msk::Unit* wg_units = nullptr;
+  const int32_t* wg_nunits = nullptr;
   int32_t* err_host = nullptr;
   std::string last_error;
 };
@@ -145,6 +146,8 @@ std::string check_config(const msk_config* c) {
   if (c->max_tokens * c->max_requests > msk::kMaxTok) return "max_tokens*max_requests must be <= 16";
   if (c->kv_capacity <= 0) return "kv_capacity must be positive";
   if (!(c->rms_eps >= 0.0f)) return "rms_eps must be >= 0";
+  if (c->expert_prefetch < 0 || c->expert_prefetch > msk::kMaxPrefetch || c->expert_prefetch > c->n_experts)
+    return "expert_prefetch must be in 0..min(32, n_experts)";
   return std::string();
 }
 
@@ -165,8 +168,7 @@ Layout make_layout(const msk_config* c, int G) {
   L.err = take(256);
   L.zeros = take(256);
   // schedule tables: units of 4 schedules + offsets (generous bound)
-  const size_t max_units = 4 * ((H / 16) * 4 + (Dq + 2 * c->n_kv_heads * c->head_dim) / 16 * 4 + (P / 16) * 4) * 2 + 64;
-  L.sched = take(max_units * sizeof(msk::Unit) + 4 * (G + 1) * sizeof(int32_t));
+  L.sched = take((size_t)G * msk::kSchCount * (msk::kMaxWgUnits * sizeof(msk::Unit) + sizeof(int32_t)));
   L.h1 = take(NT * H * 4);
   L.ssq1 = take((H / 16) * NT * 4);
   L.ssq2 = take((H / 16) * NT * 4);
@@ -237,27 +239,28 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
   SchedHost sp = build_sched_best(t_pool, H, G, &h->p_slices);
   SchedHost su = build_sched(t_unpool, 1, G);
 
-  std::vector<uint8_t> blob;
-  auto put = [&](const SchedHost& s, msk::Sched& dst) {
-    size_t at = align_up(blob.size(), 16);
-    blob.resize(at + s.units.size() * sizeof(msk::Unit));
-    if (!s.units.empty()) memcpy(blob.data() + at, s.units.data(), s.units.size() * sizeof(msk::Unit));
-    size_t at2 = align_up(blob.size(), 16);
-    blob.resize(at2 + s.off.size() * sizeof(int32_t));
-    memcpy(blob.data() + at2, s.off.data(), s.off.size() * sizeof(int32_t));
-    dst.units = reinterpret_cast<const msk::Unit*>(h->ws + lay.sched + at);
-    dst.off = reinterpret_cast<const int32_t*>(h->ws + lay.sched + at2);
-  };
+  // per-workgroup tables: units [G][kSchCount][kMaxWgUnits], counts [G][kSchCount]
+  const size_t n_units = (size_t)G * msk::kSchCount * msk::kMaxWgUnits;
+  std::vector<msk::Unit> tab(n_units, msk::Unit{0, 0, 0, 0});
+  std::vector<int32_t> cnt((size_t)G * msk::kSchCount, 0);
   const SchedHost* all[msk::kSchCount] = {&sq, &so, &sp, &su};
   for (int i = 0; i < msk::kSchCount; ++i) {
     for (int g = 0; g < G; ++g) {
-      if (all[i]->off[g + 1] - all[i]->off[g] > msk::kMaxWgUnits) {
+      const int n = all[i]->off[g + 1] - all[i]->off[g];
+      if (n > msk::kMaxWgUnits) {
         delete h;
         return fail(nullptr, MSK_E_SHAPE, "a dense schedule gives one workgroup more units than it stages");
       }
+      cnt[(size_t)g * msk::kSchCount + i] = n;
+      for (int u = 0; u < n; ++u)
+        tab[((size_t)g * msk::kSchCount + i) * msk::kMaxWgUnits + u] = all[i]->units[all[i]->off[g] + u];
     }
-    put(*all[i], h->sched[i]);
   }
+  std::vector<uint8_t> blob(n_units * sizeof(msk::Unit) + cnt.size() * sizeof(int32_t));
+  memcpy(blob.data(), tab.data(), n_units * sizeof(msk::Unit));
+  memcpy(blob.data() + n_units * sizeof(msk::Unit), cnt.data(), cnt.size() * sizeof(int32_t));
+  h->wg_units = reinterpret_cast<const msk::Unit*>(h->ws + lay.sched);
+  h->wg_nunits = reinterpret_cast<const int32_t*>(h->ws + lay.sched + n_units * sizeof(msk::Unit));
   if (blob.size() > lay.h1 - lay.sched) {
     delete h;
     return fail(nullptr, MSK_E_CAPACITY, "schedule tables exceed their workspace region");
@@ -341,6 +344,7 @@ msk_status check_io(msk_handle h, const msk_io* io) {
   if (io->trace && !aligned16(io->trace)) return fail(h, MSK_E_ALIGN, "trace must be 16-byte aligned");
   if ((io->expert_ids && !aligned16(io->expert_ids)) || (io->gates && !aligned16(io->gates)))
     return fail(h, MSK_E_ALIGN, "expert_ids/gates must be 16-byte aligned");
+  if (io->prefetch_ids && !aligned16(io->prefetch_ids)) return fail(h, MSK_E_ALIGN, "prefetch_ids must be 16-byte aligned");
   if (*h->err_host != 0) {
     int e = *h->err_host;
     *h->err_host = 0;
@@ -388,7 +392,9 @@ msk::Params base_params(msk_handle h, const msk_io* io) {
   p.accpart = reinterpret_cast<float*>(ws + L.accpart);
   p.hist = reinterpret_cast<int32_t*>(ws + L.hist);
   p.zeros = reinterpret_cast<const uint16_t*>(ws + L.zeros);
-  for (int i = 0; i < msk::kSchCount; ++i) p.sched[i] = h->sched[i];
+  p.wg_units = h->wg_units;
+  p.wg_nunits = h->wg_nunits;
+  p.n_prefetch = c.expert_prefetch;
   return p;
 }
 
@@ -425,6 +431,7 @@ extern "C" msk_status msk_verify_layer(msk_handle h, int32_t layer, const msk_io
   p.h_out = io->h_out;
   p.out_ids = io->expert_ids;
   p.out_gates = io->gates;
+  p.out_prefetch = io->prefetch_ids;
   p.trace = io->trace;
   p.trace_launch = 0;
   bool debug = false;
@@ -465,6 +472,7 @@ extern "C" msk_status msk_verify_step(msk_handle h, const msk_io* io, void* stre
     p.h_out = (l == n - 1) ? io->h_out : hb[l & 1];
     p.out_ids = io->expert_ids ? io->expert_ids + (size_t)l * NT * h->cfg.top_k : nullptr;
     p.out_gates = io->gates ? io->gates + (size_t)l * NT * h->cfg.top_k : nullptr;
+    p.out_prefetch = io->prefetch_ids ? io->prefetch_ids + (size_t)l * h->cfg.expert_prefetch : nullptr;
     p.trace = io->trace;
     p.trace_launch = l;
     hipError_t e = msk_launch_layer(p, h->grid, false, s);

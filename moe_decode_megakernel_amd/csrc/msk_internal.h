@@ -18,11 +18,12 @@ constexpr int kMaxK = 8;
 constexpr int kMaxHeadDim = 128;
 constexpr int kSubK = 128;                // dense k per wave sub-unit (4 MFMA steps of 32)
 constexpr int kAttnChunk = 64;            // keys per attention chunk in LDS
-constexpr int kTraceSlots = 23;            // phase-boundary timestamps per workgroup per launch
+constexpr int kTraceSlots = 25;            // phase-boundary timestamps per workgroup per launch
 constexpr int kG1StageBytes = 32768;       // LDS staging of GEMM1 outputs per workgroup (256 B per unit)
 constexpr int kMaxWgUnits = 32;            // dense units of one workgroup in one schedule
 constexpr int kMaxQSlices = 4;             // split-K slices of the Q projection
 constexpr int kMaxSplits = 64;             // attention splits per (request, kv head)
+constexpr int kMaxPrefetch = 32;           // experts in a speculative prefetch list
 
 // Launch modes (bit set).
 enum : uint32_t {
@@ -75,13 +76,11 @@ struct Debug {
   uint16_t* dq_dn;
 };
 
-// Schedules of the dense phases (CSR over workgroups), built once per handle.
-// A workgroup's units of every schedule are copied to LDS at launch start.
+// Schedules of the dense phases, built once per handle and stored per
+// workgroup: units [G][kSchCount][kMaxWgUnits] (unused entries zero) and
+// counts [G][kSchCount]. A workgroup copies its own rows to LDS at launch
+// start (one round trip).
 enum { kSchQkv = 0, kSchOproj, kSchPool, kSchUnpool, kSchCount };
-struct Sched {
-  const Unit* units;
-  const int32_t* off;  // [G + 1]
-};
 
 struct Params {
   // shapes
@@ -112,10 +111,13 @@ struct Params {
   float* accpart;         // [parts][NT][P]
   int32_t* hist;          // [n_layers][E] selection counts
   const uint16_t* zeros;  // 256 zero bytes (A operand of masked lanes)
-  Sched sched[kSchCount];  // QKV (own and next layer share shapes), O proj, pool, unpool
+  const Unit* wg_units;     // QKV (own and next layer share shapes), O proj, pool, unpool
+  const int32_t* wg_nunits;
+  int32_t n_prefetch;     // experts to prefetch speculatively (0 = off)
   // outputs
   int32_t* out_ids;       // [NT][k] or NULL
   float* out_gates;
+  int32_t* out_prefetch;  // [n_prefetch] or NULL: this launch's prefetch list
   Debug dbg;
   uint64_t* trace;        // [launch][grid][kTraceSlots] or NULL (self-timing variant)
   int32_t trace_launch;

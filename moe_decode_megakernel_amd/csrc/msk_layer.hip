@@ -45,6 +45,7 @@ struct Smem {
   float inv_rms[kMaxTok * kMaxReq];
   Unit units[kSchCount][kMaxWgUnits];  // this workgroup's dense units, per schedule
   int32_t nunits[kSchCount];
+  int32_t plist[kMaxPrefetch];          // speculative expert prefetch list
   int32_t flag;
 };
 
@@ -124,6 +125,21 @@ __device__ __forceinline__ int ctx_of(const Params& p, int r) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Phase-boundary slots of the self-timing trace (one uint64 per slot, per
+// workgroup, per launch; 100 MHz real-time counter).
+enum TraceSlot {
+  kTrStart = 0, kTrQkvOwn, kTrQkvOwnBar, kTrAttnQ, kTrAttnKv, kTrAttn, kTrAttnBar, kTrMerge, kTrMergeBar, kTrOprojFill, kTrOproj,
+  kTrOprojBar, kTrPoolFill, kTrRouterPool, kTrRouterPoolBar, kTrRouting, kTrGemm1, kTrGemm1Bar, kTrGemm2,
+  kTrGemm2Bar, kTrUnpoolFill, kTrUnpool, kTrUnpoolBar, kTrQkvFill, kTrQkvNext, kTrSlots
+};
+static_assert(kTrSlots == kTraceSlots, "trace slot count");
+
+// Phase-boundary stamp of the self-timing variant (row = this workgroup's
+// trace row, or NULL).
+__device__ __forceinline__ void trace_stamp(uint64_t* row, int slot) {
+  if (row && threadIdx.x == 0) row[slot] = __builtin_amdgcn_s_memrealtime();
+}
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // Pairwise tree sum over aligned groups of n lanes (n a power of two <= 64),
@@ -678,6 +694,18 @@ __device__ __forceinline__ int attn_item_base(const Params& p, const LayerW& lw,
   return base;
 }
 
+// Number of attention items of the launch (workgroups at or past it are idle
+// during the attention phase).
+__device__ __forceinline__ int attn_item_count(const Params& p, const LayerW& lw, int grid) {
+  int n = 0;
+  for (int r = 0; r < p.R; ++r) {
+    int lo, hi;
+    attn_range(p, lw, r, lo, hi);
+    n += attn_splits(p, hi - lo + 1, grid) * p.nkv;
+  }
+  return n;
+}
+
 // Partial record of (item, wave, token): o[d], then m, l (stride d + 4 floats,
 // so every record starts 16-byte aligned).
 __device__ __forceinline__ float* apart_at(const Params& p, int item, int w, int t) {
@@ -685,7 +713,7 @@ __device__ __forceinline__ float* apart_at(const Params& p, int item, int w, int
 }
 
 template <int D>
-__device__ __forceinline__ void attention_phase(const Params& p, const LayerW& lw, Smem& sm) {
+__device__ __forceinline__ void attention_phase(const Params& p, const LayerW& lw, Smem& sm, uint64_t* trace_row) {
   AttnItem it;
   if (!attn_item(p, lw, blockIdx.x, gridDim.x, it)) return;
   const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4, w = wave_id();
@@ -741,6 +769,7 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
     }
   }
 
+  trace_stamp(trace_row, kTrAttnQ);
   const float scale_log2 = rsqrtf((float)D) * 1.4426950408889634f;
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4_t o[DT];
@@ -808,6 +837,7 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
     }
     ring_fence();
     __syncthreads();
+    if (c == 0) trace_stamp(trace_row, kTrAttnKv);
     if (!active || c >= nchunks) continue;
     const int kb = it.k_begin + c * kAttnChunk;
     // scores for 4 key tiles of 16
@@ -1252,21 +1282,23 @@ struct G1Step {
   uint32_t s;  // their two E4M3 block scales (low 16 bits)
 };
 
-// Wave-uniform unit/step cursor over the wave's units u0 + w + 8*m.
-struct G1Cursor {
-  int m, st;
+// Issue cursor over a wave's (unit, step) sequence, with the lane's row
+// pointers of the current unit (recomputed once per unit).
+struct G1Issue {
+  int m, st;            // unit ordinal (wave-uniform), step in the unit
+  const uint8_t* code;  // codes of the lane's row, at the lane group's 16-byte offset
+  const uint8_t* scale; // scales of the lane's row, at the lane group's 2-byte offset
 };
 
-__device__ __forceinline__ void g1_issue(const Params& p, const Route& rt, int u, int st, G1Step& b) {
+__device__ __forceinline__ void g1_point(const Params& p, const Route& rt, int u, G1Issue& is) {
   const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4;
   const int I = p.I, P = p.P, ntile = I / 8;
   const int j = u / ntile, it = u - j * ntile;
-  const int e = rt.sel[j];
+  const int e = __builtin_amdgcn_readfirstlane(rt.sel[j]);
   const int row = r_ < 8 ? it * 8 + r_ : I + it * 8 + (r_ - 8);
-  const int k = st * 128 + g_ * 32;
   const size_t r_all = (size_t)e * (2 * I) + row;
-  b.c = *reinterpret_cast<const uint4*>(p.cur.e_gu + r_all * (P / 2) + k / 2);
-  b.s = *reinterpret_cast<const uint16_t*>(p.cur.e_gu_sc + r_all * (P / 16) + k / 16);
+  is.code = p.cur.e_gu + r_all * (P / 2) + g_ * 16;
+  is.scale = p.cur.e_gu_sc + r_all * (P / 16) + g_ * 2;
 }
 
 template <bool debug>
@@ -1283,42 +1315,50 @@ __device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
   const int total = my_units > 0 ? my_units * nsteps : 0;
   if (total > 0) {
     G1Step ring[kG1Ring];
-    G1Cursor is{0, 0};  // next step to issue
+    G1Issue is{0, 0, nullptr, nullptr};
+    g1_point(p, rt, u0 + w, is);
+    // loads of the step at the cursor; past the wave's last step the cursor
+    // stays on that step (in-bounds reloads)
     auto issue_next = [&](G1Step& slot) {
-      const bool in = is.m < my_units;
-      const int m = in ? is.m : my_units - 1, st = in ? is.st : nsteps - 1;
-      g1_issue(p, rt, u0 + w + kWaves * m, st, slot);
-      if (++is.st == nsteps) { is.st = 0; ++is.m; }
+      slot.c = *reinterpret_cast<const uint4*>(is.code + is.st * 64);
+      slot.s = *reinterpret_cast<const uint16_t*>(is.scale + is.st * 8);
+      if (is.st + 1 < nsteps) {
+        ++is.st;
+      } else if (is.m + 1 < my_units) {
+        is.st = 0;
+        ++is.m;
+        g1_point(p, rt, u0 + w + kWaves * is.m, is);
+      }
     };
 #pragma unroll
     for (int i = 0; i < kG1Ring; ++i) {
       issue_next(ring[i]);
       ring_fence();
     }
-    G1Cursor cs{0, 0};  // next step to compute
+    const uint8_t* abase = sm.x + r_ * x_stride(P) + g_ * 64;
+    int cm = 0, cst = 0;  // compute cursor
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int base = 0; base < total; base += kG1Ring) {
 #pragma unroll
       for (int i = 0; i < kG1Ring; ++i) {
         if (base + i < total) {
-          const int st = cs.st;
           uint4 bw[4];
           fp4_decode(ring[i].c, ring[i].s, bw);
-          const uint8_t* abase = sm.x + r_ * x_stride(P) + (st * 128 + g_ * 32) * 2;
+          const uint8_t* ap = abase + cst * 256;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc = mfma_f16(*reinterpret_cast<const uint4*>(abase + q * 16), bw[q], acc);
-          const int u = u0 + w + kWaves * cs.m;
-          const int j = u / ntile, it = u - j * ntile;
+          for (int q = 0; q < 4; ++q) acc = mfma_f16(*reinterpret_cast<const uint4*>(ap + q * 16), bw[q], acc);
           if constexpr (debug) {
+            const int u = u0 + w + kWaves * cm, j = u / ntile, it = u - j * ntile;
             if (p.dbg.dq_gu && rt.sel[j] == p.dbg.dq_expert) {
               const int row = r_ < 8 ? it * 8 + r_ : I + it * 8 + (r_ - 8);
-              uint4* dst = reinterpret_cast<uint4*>(p.dbg.dq_gu + (size_t)row * P + st * 128 + g_ * 32);
+              uint4* dst = reinterpret_cast<uint4*>(p.dbg.dq_gu + (size_t)row * P + cst * 128 + g_ * 32);
 #pragma unroll
               for (int q = 0; q < 4; ++q) dst[q] = bw[q];
             }
           }
-          if (st == nsteps - 1) {
-            // acc[i] = D[token 4g+i][column r]: gate (r < 8) or up (r >= 8) of i-row it*8 + (r & 7).
+          if (cst == nsteps - 1) {
+            // acc[q] = D[token 4g+q][column r]: gate (r < 8) or up (r >= 8) of i-row it*8 + (r & 7).
+            const int u = u0 + w + kWaves * cm, j = u / ntile;
             const float ts = rt.ts_gu[j];
             uint16_t* srow = reinterpret_cast<uint16_t*>(stage + (size_t)(u - u0) * 256);
 #pragma unroll
@@ -1332,8 +1372,11 @@ __device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
               }
             }
             acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            cst = 0;
+            ++cm;
+          } else {
+            ++cst;
           }
-          if (++cs.st == nsteps) { cs.st = 0; ++cs.m; }
         }
         issue_next(ring[i]);
         ring_fence();
@@ -1442,16 +1485,102 @@ __device__ __forceinline__ void gemm2_phase(const Params& p, Smem& sm) {
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-// Phase-boundary slots of the self-timing trace (one uint64 per slot, per
-// workgroup, per launch; 100 MHz real-time counter).
-enum TraceSlot {
-  kTrStart = 0, kTrQkvOwn, kTrQkvOwnBar, kTrAttn, kTrAttnBar, kTrMerge, kTrMergeBar, kTrOprojFill, kTrOproj,
-  kTrOprojBar, kTrPoolFill, kTrRouterPool, kTrRouterPoolBar, kTrRouting, kTrGemm1, kTrGemm1Bar, kTrGemm2,
-  kTrGemm2Bar, kTrUnpoolFill, kTrUnpool, kTrUnpoolBar, kTrQkvFill, kTrQkvNext, kTrSlots
-};
-static_assert(kTrSlots == kTraceSlots, "trace slot count");
 
 enum Variant { kPlain = 0, kDebug = 1, kTrace = 2 };
+
+// ---------------------------------------------------------------------------
+// Speculative expert prefetch. The layer's experts are ranked by how often the
+// previous call selected them (the routing histogram of that call, count
+// descending, index ascending) and the first n_prefetch are read once by the
+// workgroups that have no attention work, so their codes and scales are in
+// the memory-side cache when the expert phase of this launch reads them.
+// ---------------------------------------------------------------------------
+// Wave 0 writes the ranking to sm.plist (callers meet on a barrier before use).
+__device__ __forceinline__ void prefetch_rank(const Params& p, Smem& sm) {
+  if (wave_id() != 0) return;
+  const int lane = lane_id(), E = p.E, P = p.n_prefetch;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int32_t* cnt = p.hist + (size_t)p.layer * E;
+  uint32_t key[kMaxE / 64];
+#pragma unroll
+  for (int j = 0; j < kMaxE / 64; ++j) {
+    const int e = lane + j * 64;
+    // count in the high bits, 255 - e in the low byte: unique keys, larger =
+    // earlier in the ranking; 0 for e >= E (below every real key)
+    key[j] = e < E ? ((uint32_t)cnt[e] << 8) | (uint32_t)(255 - e) : 0u;
+  }
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = T | (1u << b);
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) c += popc64(__ballot(key[j] >= cand));
+    if (c >= P) T = cand;
+  }
+  // the P keys >= T, ranked by key (descending)
+  int base = 0;
+  uint32_t* scr = reinterpret_cast<uint32_t*>(&sm.red[1][0][0]);
+#pragma unroll
+  for (int j = 0; j < kMaxE / 64; ++j) {
+    const bool sel = key[j] >= T && key[j] != 0u;
+    const uint64_t m = __ballot(sel);
+    if (sel) scr[base + popc64(m & lt_mask)] = key[j];
+    base += popc64(m);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane < P) {
+    const uint32_t mine = scr[lane];
+    int rank = 0;
+    for (int q = 0; q < P; ++q) rank += scr[q] > mine ? 1 : 0;
+    sm.plist[rank] = 255 - (int)(mine & 0xFFu);
+  }
+}
+
+// Reads one dword of every 128-byte line of the listed experts' gate/up and
+// down codes and scales; the workgroup is number `idx` of `n` prefetchers.
+__device__ __forceinline__ void prefetch_experts(const Params& p, const Smem& sm, int idx, int n) {
+  const size_t I = p.I, P = p.P;
+  const size_t bytes[4] = {2 * I * P / 2, 2 * I * P / 16, P * I / 2, P * I / 16};
+  const uint8_t* base[4] = {p.cur.e_gu, p.cur.e_gu_sc, p.cur.e_dn, p.cur.e_dn_sc};
+  int lines[4], lpe = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    lines[r] = (int)((bytes[r] + 127) / 128);
+    lpe += lines[r];
+  }
+  const int total = p.n_prefetch * lpe;
+  uint32_t acc = 0;
+  for (int l0 = idx * kThreads + threadIdx.x; l0 < total; l0 += 4 * n * kThreads) {
+    uint32_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int l = min(l0 + q * n * kThreads, total - 1);
+      const int j = l / lpe;
+      int r = l - j * lpe, reg = 0;
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        if (reg == t && r >= lines[t]) { r -= lines[t]; reg = t + 1; }
+      const size_t off = min((size_t)r * 128, bytes[reg] - 4);
+      v[q] = *reinterpret_cast<const uint32_t*>(base[reg] + (size_t)sm.plist[j] * bytes[reg] + off);
+    }
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  // never true (layer >= 0); keeps the loads
+  if (p.layer < 0 && acc == 0x9E3779B9u) p.err[1] = (int32_t)acc;
+}
+
+// Copies this workgroup's units of every dense schedule to LDS (one round
+// trip; readers wait on a later workgroup barrier).
+__device__ __forceinline__ void stage_units(const Params& p, Smem& sm) {
+  constexpr int kN = kSchCount * kMaxWgUnits;
+  static_assert(kN + kSchCount <= kThreads, "one entry per thread");
+  if (threadIdx.x < kN) {
+    (&sm.units[0][0])[threadIdx.x] = p.wg_units[(size_t)blockIdx.x * kN + threadIdx.x];
+  } else if (threadIdx.x < kN + kSchCount) {
+    const int i = threadIdx.x - kN;
+    sm.nunits[i] = p.wg_nunits[(size_t)blockIdx.x * kSchCount + i];
+  }
+}
 
 template <uint32_t MODE, int VARIANT>
 __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
@@ -1470,13 +1599,8 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   const int Nqkv = Dq + 2 * p.nkv * p.d;
   DenseSlot ring[kRing];
   if (threadIdx.x == 0) sm.zero = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int sch = 0; sch < kSchCount; ++sch) {
-    const int b0 = p.sched[sch].off[blockIdx.x], n = p.sched[sch].off[blockIdx.x + 1] - b0;
-    if (threadIdx.x < n) sm.units[sch][threadIdx.x] = p.sched[sch].units[b0 + threadIdx.x];
-    if (threadIdx.x == 0) sm.nunits[sch] = n;
-  }
-  __syncthreads();
+  stage_units(p, sm);
+  if constexpr ((MODE & kModeQkvOwn) != 0) __syncthreads();
 
   if constexpr ((MODE & kModeQkvOwn) != 0) {
     dense_prefetch<Epi::Qkv>(p, kSchQkv, p.cur.w_qkv, p.H, nullptr, sm, ring);
@@ -1500,8 +1624,19 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   (void)Nqkv;
 
   // attention of the launch's layer
-  if (p.d == 128) attention_phase<128>(p, p.cur, sm);
-  else attention_phase<64>(p, p.cur, sm);
+  if (p.d == 128) attention_phase<128>(p, p.cur, sm, trace_row);
+  else attention_phase<64>(p, p.cur, sm, trace_row);
+  if (p.n_prefetch > 0) {
+    const int n_items = attn_item_count(p, p.cur, gridDim.x);
+    const bool idle = (int)blockIdx.x >= n_items;
+    if (idle || (blockIdx.x == 0 && p.out_prefetch)) {
+      prefetch_rank(p, sm);
+      __syncthreads();
+      if (blockIdx.x == 0 && p.out_prefetch && threadIdx.x < p.n_prefetch)
+        p.out_prefetch[threadIdx.x] = sm.plist[threadIdx.x];
+      if (idle) prefetch_experts(p, sm, blockIdx.x - n_items, gridDim.x - n_items);
+    }
+  }
   mark(kTrAttn);
   bar_arrive(bar);
   if (!bar_wait(bar, sm)) return;

@@ -24,7 +24,7 @@ class msk_config(ctypes.Structure):
     _fields_ = [("hidden", i32), ("n_q_heads", i32), ("n_kv_heads", i32), ("head_dim", i32),
                 ("n_experts", i32), ("top_k", i32), ("pool_dim", i32), ("expert_inter", i32),
                 ("n_layers", i32), ("max_tokens", i32), ("max_requests", i32), ("kv_capacity", i32),
-                ("rms_eps", f32), ("flags", u32)]
+                ("rms_eps", f32), ("flags", u32), ("expert_prefetch", i32)]
 
 
 LAYER_PTRS = ("w_qkv", "w_o", "w_router", "b_router", "w_pool", "w_unpool", "g_attn", "g_moe",
@@ -46,10 +46,10 @@ class msk_debug(ctypes.Structure):
 class msk_io(ctypes.Structure):
     _fields_ = [("n_requests", i32), ("n_tokens", i32), ("ctx_len", ctypes.POINTER(i32)),
                 ("h_in", vp), ("h_out", vp), ("expert_ids", vp), ("gates", vp),
-                ("debug", ctypes.POINTER(msk_debug)), ("trace", vp)]
+                ("debug", ctypes.POINTER(msk_debug)), ("prefetch_ids", vp), ("trace", vp)]
 
 
-TRACE_SLOTS = ["start", "qkv_own", "qkv_own_bar", "attn", "attn_bar", "merge", "merge_bar", "oproj_fill",
+TRACE_SLOTS = ["start", "qkv_own", "qkv_own_bar", "attn_q", "attn_kv", "attn", "attn_bar", "merge", "merge_bar", "oproj_fill",
                "oproj", "oproj_bar", "pool_fill", "router_pool", "router_pool_bar", "routing", "gemm1",
                "gemm1_bar", "gemm2", "gemm2_bar", "unpool_fill", "unpool", "unpool_bar", "qkv_fill", "qkv_next"]
 MAX_GRID = 256
@@ -129,13 +129,18 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def make_config(w, n_layers=None, max_tokens=None, max_requests=None, flags=0) -> msk_config:
+DEFAULT_EXPERT_PREFETCH = 14
+
+
+def make_config(w, n_layers=None, max_tokens=None, max_requests=None, flags=0, expert_prefetch=None) -> msk_config:
+    if expert_prefetch is None:
+        expert_prefetch = min(DEFAULT_EXPERT_PREFETCH, w.E)
     return msk_config(hidden=w.H, n_q_heads=w.nq, n_kv_heads=w.nkv, head_dim=w.d, n_experts=w.E,
                       top_k=w.k, pool_dim=w.P, expert_inter=w.I,
                       n_layers=w.n_layers if n_layers is None else n_layers,
                       max_tokens=w.T if max_tokens is None else max_tokens,
                       max_requests=w.R if max_requests is None else max_requests,
-                      kv_capacity=w.cap, rms_eps=w.eps, flags=flags)
+                      kv_capacity=w.cap, rms_eps=w.eps, flags=flags, expert_prefetch=expert_prefetch)
 
 
 def make_layer_desc(t: Dict, window: int) -> msk_layer_desc:
@@ -146,11 +151,12 @@ def make_layer_desc(t: Dict, window: int) -> msk_layer_desc:
 
 
 def make_io(n_requests, n_tokens, ctx: Sequence[int], h_in, h_out, expert_ids=None, gates=None,
-            debug: Optional[msk_debug] = None, trace=None):
+            debug: Optional[msk_debug] = None, trace=None, prefetch_ids=None):
     ctx_arr = (i32 * len(ctx))(*ctx)
     io = msk_io(n_requests=n_requests, n_tokens=n_tokens, ctx_len=ctypes.cast(ctx_arr, ctypes.POINTER(i32)),
                 h_in=_ptr(h_in), h_out=_ptr(h_out), expert_ids=_ptr(expert_ids), gates=_ptr(gates),
-                debug=ctypes.pointer(debug) if debug is not None else None, trace=_ptr(trace))
+                debug=ctypes.pointer(debug) if debug is not None else None, prefetch_ids=_ptr(prefetch_ids),
+                trace=_ptr(trace))
     io._keep = (ctx_arr, debug)
     return io
 

@@ -140,6 +140,30 @@ void orc_topk(const float* logits, int32_t n, int32_t k, int32_t* ids) {
   free(taken);
 }
 
+/* Speculative prefetch list of one layer (LMSYS post as summarised on
+ * newruntime.com, What happened: the experts the previous step used most are
+ * prefetched): count how often each expert appears in the previous step's
+ * selections ids[n_ids], then take the p experts with the largest counts,
+ * ties to the lower index. Experts with count 0 rank by index after the used
+ * ones. The count/tie rule is this build's reading. */
+void orc_prefetch_list(const int32_t* ids, int32_t n_ids, int32_t n_experts, int32_t p, int32_t* list) {
+  int32_t* count = (int32_t*)calloc((size_t)n_experts, sizeof(int32_t));
+  unsigned char* taken = (unsigned char*)calloc((size_t)n_experts, 1);
+  int32_t i, r, e;
+  for (i = 0; i < n_ids; ++i) count[ids[i]] += 1;
+  for (r = 0; r < p; ++r) {
+    int32_t best = -1;
+    for (e = 0; e < n_experts; ++e) {
+      if (taken[e]) continue;
+      if (best < 0 || count[e] > count[best]) best = e;
+    }
+    list[r] = best;
+    if (best >= 0) taken[best] = 1;
+  }
+  free(taken);
+  free(count);
+}
+
 /* Gate weights: softmax over the selected logits only. */
 void orc_gates(const float* logits, const int32_t* ids, int32_t k, double* gates) {
   double m = -INFINITY, sum = 0.0;

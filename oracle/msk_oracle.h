@@ -80,6 +80,7 @@ void orc_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, double s_ten
 float orc_dot_canon_f32(const float* x, const float* w, int32_t n);
 void orc_topk(const float* logits, int32_t n, int32_t k, int32_t* ids);
 void orc_gates(const float* logits, const int32_t* ids, int32_t k, double* gates);
+void orc_prefetch_list(const int32_t* ids, int32_t n_ids, int32_t n_experts, int32_t p, int32_t* list);
 void orc_rmsnorm(const double* x, const uint16_t* g, int32_t n, double eps, double* y);
 double orc_silu(double x);
 void orc_attention(const double* q, const uint16_t* k_cache, const uint16_t* v_cache,

@@ -55,6 +55,7 @@ def lib():
         L.orc_dot_canon_f32.restype = c_f32
         L.orc_topk.argtypes = [vp, c_i32, c_i32, vp]
         L.orc_gates.argtypes = [vp, vp, c_i32, vp]
+        L.orc_prefetch_list.argtypes = [vp, c_i32, c_i32, c_i32, vp]
         L.orc_rmsnorm.argtypes = [vp, vp, c_i32, c_f64, vp]
         L.orc_silu.argtypes = [c_f64]
         L.orc_silu.restype = c_f64
@@ -121,6 +122,14 @@ def gates(logits, ids):
     g = np.empty(ids.size, np.float64)
     lib().orc_gates(_p(lg), _p(ids), ids.size, _p(g))
     return g
+
+
+def prefetch_list(ids, n_experts, p):
+    """Top-p experts by selection count in ids (count desc, index asc)."""
+    ids = np.ascontiguousarray(ids, np.int32).ravel()
+    out = np.empty(p, np.int32)
+    lib().orc_prefetch_list(_p(ids), ids.size, n_experts, p, _p(out))
+    return out
 
 
 def rmsnorm(x, g_bf16, eps):

@@ -174,3 +174,17 @@ def test_silu_closed_forms():
     assert abs(orc.silu(-40.0)) < 1e-15
     # silu(ln 3) = ln 3 * 3/4 (sigma(ln 3) = 3/4)
     assert abs(orc.silu(math.log(3.0)) - 0.75 * math.log(3.0)) < 1e-15
+
+
+def test_prefetch_list_matches_bruteforce_sort():
+    """Top-p by (count desc, index asc) against numpy's stable lexsort of the
+    bincount (a library routine), on random selections and on constructed ties."""
+    rng = np.random.default_rng(5)
+    for E, p, n in [(256, 14, 128), (16, 14, 32), (64, 8, 40), (256, 14, 0)]:
+        ids = rng.integers(0, E, size=n).astype(np.int32)
+        cnt = np.bincount(ids, minlength=E)
+        ref = np.lexsort((np.arange(E), -cnt))[:p]
+        assert np.array_equal(orc.prefetch_list(ids, E, p), ref)
+    # hand case: counts 3,3,1 at experts 7,2,5 -> [2, 7, 5, then unused 0, 1, ...]
+    ids = np.array([7, 2, 7, 2, 5, 7, 2], np.int32)
+    assert orc.prefetch_list(ids, 10, 6).tolist() == [2, 7, 5, 0, 1, 3]
