@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-layers", default="0,1,2,3,4,5,6,7", help="layers of the step the oracle times")
     ap.add_argument("--trace", action="store_true",
                     help="after timing, run one step with the self-timing kernel and print the phase breakdown")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each step's msk_verify_step in a HIP graph and time the replays")
     ap.add_argument("--expert-prefetch", type=int, default=None,
                     help="experts per layer to prefetch speculatively (default 14; 0 = off)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -133,11 +135,30 @@ def main():
     ctx = [w.ctx] * w.R
     ios = [msk.make_io(w.R, w.T, ctx, h_in[s], h_out, ids[s], gates[s]) for s in range(nsteps)]
 
-    def run(s):
+    def eager(s):
         if w.n_layers == 1:
             handle.verify_layer(0, ios[s])
         else:
             handle.verify_step(ios[s])
+
+    run = eager
+    if args.graph:
+        # one graph per step input (each captures the reset launch, the layer
+        # launches and the error-word copy of one call)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            eager(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for s_ in range(nsteps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                eager(s_)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        run = lambda s_: graphs[s_].replay()  # noqa: E731
 
     for s in range(args.warmup):
         run(s)
@@ -199,6 +220,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
+        "launch": "hip graph per step" if args.graph else "eager (62 launches per step)",
         "config": {
             "workload": w.name, "layers": w.n_layers, "tokens_per_request": w.T, "requests": w.R,
             "ctx": w.ctx, "windows": "2048 (46 layers) / global (16 layers)" if w.n_layers == 62 else w.windows[0],

@@ -93,3 +93,25 @@ def routing_margins(logits, k):
     """Per token: gap between the k-th and (k+1)-th largest logit."""
     s = -np.sort(-np.asarray(logits, np.float64), axis=1)
     return s[:, k - 1] - s[:, k]
+
+
+def routing_mismatches(gpu_ids, logits, k, thr):
+    """Tokens whose GPU selection disagrees with the oracle's logits beyond
+    near-ties: the selected set must equal the oracle's top-k wherever the
+    k-th/(k+1)-th margin exceeds thr, and consecutive GPU ranks must not
+    invert two logits that differ by more than thr (the ranking is by value,
+    ties to the lower index; values closer than thr may legitimately swap)."""
+    bad = []
+    lg_all = np.asarray(logits, np.float64)
+    for t in range(lg_all.shape[0]):
+        lg = lg_all[t]
+        ref = np.lexsort((np.arange(lg.size), -lg))[:k]
+        s = -np.sort(-lg)
+        margin = s[k - 1] - s[k]
+        ids = np.asarray(gpu_ids[t])
+        if margin > thr and set(ids.tolist()) != set(ref.tolist()):
+            bad.append(t)
+            continue
+        if any(lg[ids[r + 1]] - lg[ids[r]] > thr for r in range(k - 1)):
+            bad.append(t)
+    return bad

@@ -5,7 +5,7 @@ import pytest
 
 from moe_decode_megakernel_amd import msk, synth
 from oracle import oracle as orc
-from tests.helpers import bf16_to_f64, rel_err, routing_margins, say
+from tests.helpers import bf16_to_f64, rel_err, routing_margins, routing_mismatches, say
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def test_small_stack_step_matches_oracle_chain():
         hh, st = orc.layer_forward(w, layers[l], w.R, w.T, [w.ctx], hh, k, v, w.cap, eps=w.eps)
         m = routing_margins(st["logits"], w.k)
         say(f"[stack4] layer {l}: min routing margin {m.min():.2e}")
-        assert np.array_equal(g["ids"][l], st["ids"]), f"layer {l} routing differs"
+        assert not routing_mismatches(g["ids"][l], st["logits"], w.k, 1e-3), f"layer {l} routing differs"
         rows = slice(w.ctx, w.ctx + w.T)
         assert rel_err(bf16_to_f64(g["k"][l][:, :, rows]), bf16_to_f64(k[:, :, rows])) < TOL
         assert np.array_equal(g["k"][l][:, :, :w.ctx], caches[l][0][:, :, :w.ctx])
