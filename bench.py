@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="step62",
-                    choices=["step62", "swa_layer", "global_layer", "tiny_swa"])
+                    choices=["step62", "batch4_step62", "swa_layer", "global_layer", "tiny_swa"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", default="0,1,2,3,4,5,6,7", help="layers of the step the oracle times")
     ap.add_argument("--trace", action="store_true",

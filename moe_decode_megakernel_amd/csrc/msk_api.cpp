@@ -111,6 +111,7 @@ struct msk_handle_s {
   const msk::Unit* wg_units = nullptr;
   const int32_t* wg_nunits = nullptr;
   int32_t* err_host = nullptr;
+  uint64_t calls = 0;  // verify calls enqueued (selects the histogram buffers)
   std::string last_error;
 };
 
@@ -143,7 +144,6 @@ std::string check_config(const msk_config* c) {
   if (c->n_layers <= 0) return "n_layers must be positive";
   if (c->max_tokens <= 0 || c->max_tokens > msk::kMaxTok) return "max_tokens must be in 1..16";
   if (c->max_requests <= 0 || c->max_requests > msk::kMaxReq) return "max_requests must be in 1..4";
-  if (c->max_tokens * c->max_requests > msk::kMaxTok) return "max_tokens*max_requests must be <= 16";
   if (c->kv_capacity <= 0) return "kv_capacity must be positive";
   if (!(c->rms_eps >= 0.0f)) return "rms_eps must be >= 0";
   if (c->expert_prefetch < 0 || c->expert_prefetch > msk::kMaxPrefetch || c->expert_prefetch > c->n_experts)
@@ -151,8 +151,15 @@ std::string check_config(const msk_config* c) {
   return std::string();
 }
 
+// A call runs its requests in passes of at most kMaxTok tokens (one 16-row
+// MFMA tile): requests_per_pass whole requests each.
+int requests_per_pass(int32_t tokens) { return std::max(1, msk::kMaxTok / std::max(1, tokens)); }
+int pass_tokens(const msk_config* c) {
+  return std::min(c->max_requests, requests_per_pass(c->max_tokens)) * c->max_tokens;
+}
+
 Layout make_layout(const msk_config* c, int G) {
-  const size_t NT = (size_t)c->max_tokens * c->max_requests;
+  const size_t NT = (size_t)pass_tokens(c);
   const size_t H = c->hidden, Dq = (size_t)c->n_q_heads * c->head_dim, P = c->pool_dim, I = c->expert_inter;
   const size_t E = c->n_experts, K = c->top_k;
   const size_t nsel = std::min(E, NT * K);
@@ -181,7 +188,7 @@ Layout make_layout(const msk_config* c, int G) {
   L.ppart = take(4 * NT * P * 4);
   L.abuf = take(nsel * NT * I * 2);
   L.accpart = take(parts * NT * P * 4);
-  L.hist = take((size_t)c->n_layers * E * 4);
+  L.hist = take(2 * (size_t)c->n_layers * E * 4);  // by call parity: previous call's counts | this call's
   L.total = o;
   return L;
 }
@@ -208,7 +215,7 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
   if (cfg->n_experts > G) return fail(nullptr, MSK_E_SHAPE, "n_experts exceeds the workgroups of one launch (one router expert per workgroup)");
   {
     // GEMM1 stages 256 B per (selected expert, 8-row i-tile) unit of a workgroup in LDS
-    const int64_t nsel = std::min<int64_t>(cfg->n_experts, (int64_t)cfg->max_tokens * cfg->max_requests * cfg->top_k);
+    const int64_t nsel = std::min<int64_t>(cfg->n_experts, (int64_t)pass_tokens(cfg) * cfg->top_k);
     const int64_t units = nsel * (cfg->expert_inter / 8);
     if ((units + G - 1) / G * 256 > msk::kG1StageBytes)
       return fail(nullptr, MSK_E_SHAPE, "too many expert units per workgroup for the GEMM1 staging area");
@@ -270,11 +277,11 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
     return fail(nullptr, MSK_E_HIP, "hipMemcpy of the schedule tables failed");
   }
   // zero the barrier word, error word and routing histogram once
-  std::vector<uint8_t> zeros(std::max<size_t>(256, (size_t)cfg->n_layers * cfg->n_experts * 4), 0);
+  std::vector<uint8_t> zeros(std::max<size_t>(256, 2 * (size_t)cfg->n_layers * cfg->n_experts * 4), 0);
   if (hipMemcpy(h->ws + lay.bar, zeros.data(), 256, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(h->ws + lay.err, zeros.data(), 256, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(h->ws + lay.zeros, zeros.data(), 256, hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(h->ws + lay.hist, zeros.data(), (size_t)cfg->n_layers * cfg->n_experts * 4, hipMemcpyHostToDevice) != hipSuccess) {
+      hipMemcpy(h->ws + lay.hist, zeros.data(), 2 * (size_t)cfg->n_layers * cfg->n_experts * 4, hipMemcpyHostToDevice) != hipSuccess) {
     delete h;
     return fail(nullptr, MSK_E_HIP, "hipMemcpy of the workspace header failed");
   }
@@ -390,7 +397,13 @@ msk::Params base_params(msk_handle h, const msk_io* io) {
   p.ppart = reinterpret_cast<float*>(ws + L.ppart);
   p.abuf = reinterpret_cast<uint16_t*>(ws + L.abuf);
   p.accpart = reinterpret_cast<float*>(ws + L.accpart);
-  p.hist = reinterpret_cast<int32_t*>(ws + L.hist);
+  {
+    int32_t* hist = reinterpret_cast<int32_t*>(ws + L.hist);
+    const size_t n = (size_t)c.n_layers * c.n_experts;
+    p.hist_wr = hist + (h->calls & 1) * n;
+    p.hist_rd = hist + ((h->calls + 1) & 1) * n;
+    p.hist_add = 0;
+  }
   p.zeros = reinterpret_cast<const uint16_t*>(ws + L.zeros);
   p.wg_units = h->wg_units;
   p.wg_nunits = h->wg_nunits;
@@ -414,37 +427,83 @@ msk_status finish(msk_handle h, hipStream_t s) {
 
 }  // namespace
 
+namespace {
+
+// Pointer to request r0's slice of a [R][nkv][cap][d] cache.
+uint16_t* cache_at(uint16_t* base, int r0, const msk_config& c) {
+  return base + (size_t)r0 * c.n_kv_heads * c.kv_capacity * c.head_dim;
+}
+
+msk::LayerW layer_for_pass(const msk_layer_desc& d, int r0, const msk_config& c) {
+  msk::LayerW w = to_w(d);
+  w.k_cache = cache_at(d.k_cache, r0, c);
+  w.v_cache = cache_at(d.v_cache, r0, c);
+  return w;
+}
+
+// Enqueues one verify call: layers [l0, l1) of the step (one launch each; the
+// first launch also projects its own layer's QKV), run for the requests in
+// passes of at most 16 tokens. Pass outputs go to the requests' own rows.
+msk_status run_call(msk_handle h, int l0, int l1, const msk_io* io, hipStream_t s, bool debug) {
+  const msk_config& c = h->cfg;
+  const Layout& L = h->lay;
+  const int T = io->n_tokens, R = io->n_requests, NT_all = R * T, K = c.top_k, H = c.hidden;
+  const int rpp = requests_per_pass(T);
+  const int n = l1 - l0;
+  if ((io->debug || io->trace) && R > rpp)
+    return fail(h, MSK_E_INVALID, "debug dumps and the trace need all tokens of the call in one 16-token pass");
+  float* hb[2] = {reinterpret_cast<float*>(h->ws + L.hbuf0), reinterpret_cast<float*>(h->ws + L.hbuf1)};
+  if (msk_launch_reset(reinterpret_cast<uint32_t*>(h->ws + L.bar), reinterpret_cast<int32_t*>(h->ws + L.err), s) !=
+      hipSuccess)
+    return fail(h, MSK_E_HIP, "reset launch failed");
+  uint32_t base = 0;
+  for (int r0 = 0; r0 < R; r0 += rpp) {
+    const int nr = std::min(rpp, R - r0);
+    for (int i = 0; i < n; ++i) {
+      const int l = l0 + i;
+      msk::Params p = base_params(h, io);
+      p.R = nr;
+      p.NT = nr * T;
+      for (int r = 0; r < msk::kMaxReq; ++r) p.ctx[r] = r < nr ? io->ctx_len[r0 + r] : 0;
+      p.mode = (i == 0 ? msk::kModeQkvOwn : 0u) | (i + 1 < n ? msk::kModeQkvNext : 0u);
+      p.layer = l;
+      p.bar_base = base;
+      p.cur = layer_for_pass(h->layers[l], r0, c);
+      p.nxt = (i + 1 < n) ? layer_for_pass(h->layers[l + 1], r0, c) : p.cur;
+      p.h_in = (i == 0) ? io->h_in + (size_t)r0 * T * H : hb[(i - 1) & 1];
+      p.h_out = (i == n - 1) ? io->h_out + (size_t)r0 * T * H : hb[i & 1];
+      const size_t row0 = (size_t)i * NT_all * K + (size_t)r0 * T * K;
+      p.out_ids = io->expert_ids ? io->expert_ids + row0 : nullptr;
+      p.out_gates = io->gates ? io->gates + row0 : nullptr;
+      // the speculative prefetch runs in the first pass, from the previous call's counts
+      p.n_prefetch = r0 == 0 ? c.expert_prefetch : 0;
+      p.out_prefetch = (r0 == 0 && io->prefetch_ids) ? io->prefetch_ids + (size_t)i * c.expert_prefetch : nullptr;
+      p.hist_add = r0 > 0;
+      p.trace = io->trace;
+      p.trace_launch = i;
+      if (debug) {
+        const msk_debug& d = *io->debug;
+        p.dbg = msk::Debug{d.q, d.k_new, d.v_new, d.attn, d.h1, d.n2, d.logits, d.p, d.acc,
+                           d.dq_expert, d.dq_gate_up, d.dq_down};
+      }
+      hipError_t e = msk_launch_layer(p, h->grid, debug, s);
+      if (e != hipSuccess) return fail(h, MSK_E_HIP, std::string("layer launch failed: ") + hipGetErrorString(e));
+      base += barriers_of(p.mode);
+    }
+  }
+  h->calls += 1;
+  return finish(h, s);
+}
+
+}  // namespace
+
 extern "C" msk_status msk_verify_layer(msk_handle h, int32_t layer, const msk_io* io, void* stream) {
   if (!h) return fail(nullptr, MSK_E_INVALID, "handle is NULL");
   if (layer < 0 || layer >= h->cfg.n_layers) return fail(h, MSK_E_INVALID, "layer out of range");
   if (!h->loaded[layer]) return fail(h, MSK_E_STATE, "layer not loaded");
   msk_status st = check_io(h, io);
   if (st != MSK_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  msk::Params p = base_params(h, io);
-  p.mode = msk::kModeQkvOwn;
-  p.layer = layer;
-  p.bar_base = 0;
-  p.cur = to_w(h->layers[layer]);
-  p.nxt = p.cur;
-  p.h_in = io->h_in;
-  p.h_out = io->h_out;
-  p.out_ids = io->expert_ids;
-  p.out_gates = io->gates;
-  p.out_prefetch = io->prefetch_ids;
-  p.trace = io->trace;
-  p.trace_launch = 0;
-  bool debug = false;
-  if (io->debug) {
-    const msk_debug& d = *io->debug;
-    p.dbg = msk::Debug{d.q, d.k_new, d.v_new, d.attn, d.h1, d.n2, d.logits, d.p, d.acc,
-                       d.dq_expert, d.dq_gate_up, d.dq_down};
-    debug = true;
-  }
-  if (msk_launch_reset(p.bar, p.err, s) != hipSuccess) return fail(h, MSK_E_HIP, "reset launch failed");
-  hipError_t e = msk_launch_layer(p, h->grid, debug, s);
-  if (e != hipSuccess) return fail(h, MSK_E_HIP, std::string("layer launch failed: ") + hipGetErrorString(e));
-  return finish(h, s);
+  return run_call(h, layer, layer + 1, io, (hipStream_t)stream, io->debug != nullptr);
 }
 
 extern "C" msk_status msk_verify_step(msk_handle h, const msk_io* io, void* stream) {
@@ -453,33 +512,8 @@ extern "C" msk_status msk_verify_step(msk_handle h, const msk_io* io, void* stre
     if (!h->loaded[l]) return fail(h, MSK_E_STATE, "not every layer is loaded");
   msk_status st = check_io(h, io);
   if (st != MSK_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  const Layout& L = h->lay;
-  const int n = h->cfg.n_layers;
-  const int NT = io->n_requests * io->n_tokens;
-  float* hb[2] = {reinterpret_cast<float*>(h->ws + L.hbuf0), reinterpret_cast<float*>(h->ws + L.hbuf1)};
-  if (msk_launch_reset(reinterpret_cast<uint32_t*>(h->ws + L.bar), reinterpret_cast<int32_t*>(h->ws + L.err), s) != hipSuccess)
-    return fail(h, MSK_E_HIP, "reset launch failed");
-  uint32_t base = 0;
-  for (int l = 0; l < n; ++l) {
-    msk::Params p = base_params(h, io);
-    p.mode = (l == 0 ? msk::kModeQkvOwn : 0u) | (l + 1 < n ? msk::kModeQkvNext : 0u);
-    p.layer = l;
-    p.bar_base = base;
-    p.cur = to_w(h->layers[l]);
-    p.nxt = (l + 1 < n) ? to_w(h->layers[l + 1]) : p.cur;
-    p.h_in = (l == 0) ? io->h_in : hb[(l - 1) & 1];
-    p.h_out = (l == n - 1) ? io->h_out : hb[l & 1];
-    p.out_ids = io->expert_ids ? io->expert_ids + (size_t)l * NT * h->cfg.top_k : nullptr;
-    p.out_gates = io->gates ? io->gates + (size_t)l * NT * h->cfg.top_k : nullptr;
-    p.out_prefetch = io->prefetch_ids ? io->prefetch_ids + (size_t)l * h->cfg.expert_prefetch : nullptr;
-    p.trace = io->trace;
-    p.trace_launch = l;
-    hipError_t e = msk_launch_layer(p, h->grid, false, s);
-    if (e != hipSuccess) return fail(h, MSK_E_HIP, std::string("layer launch failed: ") + hipGetErrorString(e));
-    base += barriers_of(p.mode);
-  }
-  return finish(h, s);
+  if (io->debug) return fail(h, MSK_E_INVALID, "debug dumps are honoured by msk_verify_layer only");
+  return run_call(h, 0, h->cfg.n_layers, io, (hipStream_t)stream, false);
 }
 
 extern "C" msk_status msk_destroy(msk_handle h) {

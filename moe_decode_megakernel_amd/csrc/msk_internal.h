@@ -109,7 +109,9 @@ struct Params {
   float* ppart;           // [p_slices][NT][P]
   uint16_t* abuf;         // f16 [n_sel_max][NT][I]
   float* accpart;         // [parts][NT][P]
-  int32_t* hist;          // [n_layers][E] selection counts
+  const int32_t* hist_rd; // [n_layers][E] selection counts of the previous call (prefetch ranking)
+  int32_t* hist_wr;       // [n_layers][E] this call's counts
+  int32_t hist_add;       // add to hist_wr (later token passes of a call) instead of overwriting
   const uint16_t* zeros;  // 256 zero bytes (A operand of masked lanes)
   const Unit* wg_units;     // QKV (own and next layer share shapes), O proj, pool, unpool
   const int32_t* wg_nunits;

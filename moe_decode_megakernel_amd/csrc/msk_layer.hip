@@ -1236,7 +1236,10 @@ __device__ __forceinline__ void routing(const Params& p, Smem& sm, bool write_ou
       if (p.out_gates) p.out_gates[t * K + r] = rt.gates[t][r];
     }
   }
-  if (write_out && p.hist && threadIdx.x < E) p.hist[(size_t)p.layer * E + threadIdx.x] = rt.count[threadIdx.x];
+  if (write_out && p.hist_wr && threadIdx.x < E) {
+    int32_t* hw = p.hist_wr + (size_t)p.layer * E + threadIdx.x;
+    *hw = rt.count[threadIdx.x] + (p.hist_add ? *hw : 0);
+  }
   __syncthreads();
 }
 
@@ -1500,7 +1503,7 @@ __device__ __forceinline__ void prefetch_rank(const Params& p, Smem& sm) {
   if (wave_id() != 0) return;
   const int lane = lane_id(), E = p.E, P = p.n_prefetch;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int32_t* cnt = p.hist + (size_t)p.layer * E;
+  const int32_t* cnt = p.hist_rd + (size_t)p.layer * E;
   uint32_t key[kMaxE / 64];
 #pragma unroll
   for (int j = 0; j < kMaxE / 64; ++j) {
