@@ -269,6 +269,45 @@ __device__ __forceinline__ void compute_inv_rms(const Params& p, const float* h,
   __syncthreads();
 }
 
+// inv_rms from per-tile partial sums of squares in two steps, so the loads can
+// be issued early: lane j of wave w holds partials j, j+64, j+128, j+192 of
+// tokens w and w+8 (summed in that order, then pairwise halving over lanes).
+struct SsqLoads {
+  float v[kMaxTok / kWaves][4];
+};
+static_assert(kMaxTok / kWaves == 2, "two tokens per wave");
+
+__device__ __forceinline__ SsqLoads ssq_issue(const Params& p, const float* ssq) {
+  SsqLoads L;
+  const int lane = lane_id(), w = wave_id(), NT = p.NT, nt = p.H / 16;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int t = min(w + r * kWaves, NT - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) L.v[r][q] = ssq[min(lane + q * 64, nt - 1) * NT + t];
+  }
+  return L;
+}
+
+// Writes sm.inv_rms (the caller meets on a workgroup barrier before use).
+__device__ __forceinline__ void ssq_finish(const Params& p, const SsqLoads& L, Smem& sm) {
+  const int lane = lane_id(), w = wave_id(), NT = p.NT, nt = p.H / 16;
+  if (!p.use_norm) {
+    if (threadIdx.x < kMaxTok) sm.inv_rms[threadIdx.x] = 1.0f;
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int t = w + r * kWaves;
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (lane + q * 64 < nt) s += L.v[r][q];
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0 && t < NT) sm.inv_rms[t] = rsqrtf(s / (float)p.H + p.eps);
+  }
+}
+
 // X = fp16(h * inv_rms * g), or fp16(h * g) when the caller applies inv_rms to
 // the projection's output instead (with_inv = false), or fp16(h) without the
 // norm; rounded to nearest even. Item i = (token i / K8, elements 8*(i % K8)
@@ -276,6 +315,7 @@ __device__ __forceinline__ void compute_inv_rms(const Params& p, const float* h,
 // size), and the loads of kFillBatch items are issued before any is used.
 constexpr int kFillBatch = 4;
 
+template <int B = kFillBatch>
 __device__ __forceinline__ void fill_x_norm(const Params& p, const float* h, const uint16_t* g, Smem& sm,
                                             bool with_inv = true) {
   const int K = p.H, NT = p.NT, K8 = K / 8;
@@ -288,17 +328,17 @@ __device__ __forceinline__ void fill_x_norm(const Params& p, const float* h, con
 #pragma unroll
     for (int j = 0; j < 8; ++j) gj[j] = p.use_norm ? bf2f((uint16_t)(gw[j >> 1] >> ((j & 1) * 16))) : 1.0f;
   }
-  for (int i0 = threadIdx.x; i0 < total; i0 += kFillBatch * kThreads) {
-    float4 a[kFillBatch], b[kFillBatch];
+  for (int i0 = threadIdx.x; i0 < total; i0 += B * kThreads) {
+    float4 a[B], b[B];
 #pragma unroll
-    for (int q = 0; q < kFillBatch; ++q) {
+    for (int q = 0; q < B; ++q) {
       const int t = min((i0 + q * kThreads) / K8, NT - 1);
       const float4* hp = reinterpret_cast<const float4*>(h + (size_t)t * K + k);
       a[q] = hp[0];
       b[q] = hp[1];
     }
 #pragma unroll
-    for (int q = 0; q < kFillBatch; ++q) {
+    for (int q = 0; q < B; ++q) {
       const int i = i0 + q * kThreads;
       if (i >= total) break;
       const int t = i / K8;
@@ -327,33 +367,9 @@ __device__ __forceinline__ void fill_x_norm(const Params& p, const float* h, con
 // partial sums are requested before the fill so both round trips overlap.
 __device__ __forceinline__ void fill_x_qkv(const Params& p, const float* h, const uint16_t* g, const float* ssq,
                                            Smem& sm) {
-  const int lane = lane_id(), w = wave_id(), NT = p.NT, H = p.H;
-  const int nt = H / 16;
-  float v[2][4];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int t = min(w + r * kWaves, NT - 1);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = min(lane + q * 64, nt - 1);
-      v[r][q] = ssq[i * NT + t];
-    }
-  }
-  fill_x_norm(p, h, g, sm, false);
-  if (p.use_norm) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int t = w + r * kWaves;
-      float s = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (lane + q * 64 < nt) s += v[r][q];
-      for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-      if (lane == 0 && t < NT) sm.inv_rms[t] = rsqrtf(s / (float)H + p.eps);
-    }
-  } else if (threadIdx.x < kMaxTok) {
-    sm.inv_rms[threadIdx.x] = 1.0f;
-  }
+  const SsqLoads L = ssq_issue(p, ssq);
+  fill_x_norm<2 * kFillBatch>(p, h, g, sm, false);
+  ssq_finish(p, L, sm);
   __syncthreads();
 }
 
@@ -382,21 +398,22 @@ __device__ __forceinline__ void fill_x_copy(const uint16_t* src, int K, int NT, 
 }
 
 // X = sum over n partial slots of fp32 [n][NT][K] (slot order), rounded to fp16.
+template <int B = kFillBatch>
 __device__ __forceinline__ void fill_x_sum(const float* parts, int n, int K, int NT, Smem& sm) {
   const int K8 = K / 8, total = kMaxTok * K8;
-  for (int i0 = threadIdx.x; i0 < total; i0 += kFillBatch * kThreads) {
-    float v[kFillBatch][8];
+  for (int i0 = threadIdx.x; i0 < total; i0 += B * kThreads) {
+    float v[B][8];
 #pragma unroll
-    for (int q = 0; q < kFillBatch; ++q)
+    for (int q = 0; q < B; ++q)
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[q][j] = 0.0f;
     int s = 0;
     for (; s + 2 <= n; s += 2) {
-      float4 a[2][kFillBatch], b[2][kFillBatch];
+      float4 a[2][B], b[2][B];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int q = 0; q < kFillBatch; ++q) {
+        for (int q = 0; q < B; ++q) {
           const int i = i0 + q * kThreads;
           const int t = min(i / K8, NT - 1), k = (i % K8) * 8;
           const float4* src = reinterpret_cast<const float4*>(parts + ((size_t)(s + u) * NT + t) * K + k);
@@ -406,15 +423,15 @@ __device__ __forceinline__ void fill_x_sum(const float* parts, int n, int K, int
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int q = 0; q < kFillBatch; ++q) {
+        for (int q = 0; q < B; ++q) {
           v[q][0] += a[u][q].x; v[q][1] += a[u][q].y; v[q][2] += a[u][q].z; v[q][3] += a[u][q].w;
           v[q][4] += b[u][q].x; v[q][5] += b[u][q].y; v[q][6] += b[u][q].z; v[q][7] += b[u][q].w;
         }
     }
     if (s < n) {
-      float4 a[kFillBatch], b[kFillBatch];
+      float4 a[B], b[B];
 #pragma unroll
-      for (int q = 0; q < kFillBatch; ++q) {
+      for (int q = 0; q < B; ++q) {
         const int i = i0 + q * kThreads;
         const int t = min(i / K8, NT - 1), k = (i % K8) * 8;
         const float4* src = reinterpret_cast<const float4*>(parts + ((size_t)s * NT + t) * K + k);
@@ -422,13 +439,13 @@ __device__ __forceinline__ void fill_x_sum(const float* parts, int n, int K, int
         b[q] = src[1];
       }
 #pragma unroll
-      for (int q = 0; q < kFillBatch; ++q) {
+      for (int q = 0; q < B; ++q) {
         v[q][0] += a[q].x; v[q][1] += a[q].y; v[q][2] += a[q].z; v[q][3] += a[q].w;
         v[q][4] += b[q].x; v[q][5] += b[q].y; v[q][6] += b[q].z; v[q][7] += b[q].w;
       }
     }
 #pragma unroll
-    for (int q = 0; q < kFillBatch; ++q) {
+    for (int q = 0; q < B; ++q) {
       const int i = i0 + q * kThreads;
       if (i >= total) break;
       const int t = i / K8, k = (i % K8) * 8;
@@ -730,46 +747,6 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
   uint16_t* Ks = reinterpret_cast<uint16_t*>(sm.x);
   uint16_t* Vt = Ks + kAttnChunk * RS;
 
-  // Q^T operand: col = token r_, 8 consecutive dims per lane group, summed over slices.
-  // Q^T operand: all split-K slices of Q are requested at once (one round
-  // trip; lanes of inactive waves or tokens read an in-range row and are
-  // zeroed), then summed in slice order.
-  uint4 qb[KS];
-  {
-    const int tok = it.r * p.T + min(r_, p.T - 1);
-    const int hq = active ? h : it.g * group;
-    float4 qa[kMaxQSlices][KS], qc[kMaxQSlices][KS];
-#pragma unroll
-    for (int sl = 0; sl < kMaxQSlices; ++sl) {
-      const int slc = min(sl, p.q_slices - 1);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const float4* q4 = reinterpret_cast<const float4*>(
-            p.qpart + ((size_t)slc * p.NT + tok) * Dq + hq * D + s * 32 + g_ * 8);
-        qa[sl][s] = q4[0];
-        qc[sl][s] = q4[1];
-      }
-    }
-    const bool use = active && r_ < p.T;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int sl = 0; sl < kMaxQSlices; ++sl) {
-        if (sl < p.q_slices) {
-          const float4 a = qa[sl][s], b = qc[sl][s];
-          v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-          v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
-        }
-      }
-      qb[s].x = use ? pack2(f2h(v[0]), f2h(v[1])) : 0u;
-      qb[s].y = use ? pack2(f2h(v[2]), f2h(v[3])) : 0u;
-      qb[s].z = use ? pack2(f2h(v[4]), f2h(v[5])) : 0u;
-      qb[s].w = use ? pack2(f2h(v[6]), f2h(v[7])) : 0u;
-    }
-  }
-
-  trace_stamp(trace_row, kTrAttnQ);
   const float scale_log2 = rsqrtf((float)D) * 1.4426950408889634f;
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4_t o[DT];
@@ -823,6 +800,46 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
   ring_fence();
   load_chunk(1, kreg1, vreg1);
   ring_fence();
+  // Q^T operand (col = token r_, 8 consecutive dims per lane group): all
+  // split-K slices of Q are requested right after the first two K/V chunks
+  // (one round trip for both; lanes of inactive waves or tokens read an
+  // in-range row and are zeroed), then summed in slice order.
+  uint4 qb[KS];
+  {
+    const int tok = it.r * p.T + min(r_, p.T - 1);
+    const int hq = active ? h : it.g * group;
+    float4 qa[kMaxQSlices][KS], qc[kMaxQSlices][KS];
+#pragma unroll
+    for (int sl = 0; sl < kMaxQSlices; ++sl) {
+      const int slc = min(sl, p.q_slices - 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const float4* q4 = reinterpret_cast<const float4*>(
+            p.qpart + ((size_t)slc * p.NT + tok) * Dq + hq * D + s * 32 + g_ * 8);
+        qa[sl][s] = q4[0];
+        qc[sl][s] = q4[1];
+      }
+    }
+    const bool use = active && r_ < p.T;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int sl = 0; sl < kMaxQSlices; ++sl) {
+        if (sl < p.q_slices) {
+          const float4 a = qa[sl][s], b = qc[sl][s];
+          v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+          v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+        }
+      }
+      qb[s].x = use ? pack2(f2h(v[0]), f2h(v[1])) : 0u;
+      qb[s].y = use ? pack2(f2h(v[2]), f2h(v[3])) : 0u;
+      qb[s].z = use ? pack2(f2h(v[4]), f2h(v[5])) : 0u;
+      qb[s].w = use ? pack2(f2h(v[6]), f2h(v[7])) : 0u;
+    }
+  }
+
+  trace_stamp(trace_row, kTrAttnQ);
   for (int c0 = 0; c0 < nchunks; c0 += 2) {
 #pragma unroll
    for (int half = 0; half < 2; ++half) {
@@ -974,8 +991,10 @@ __device__ __forceinline__ void merge_phase(const Params& p, const LayerW& lw) {
 //   k = 8j .. 8j+7 ascending and the partials combined pairwise, adjacent
 //   pairs first.
 // Thread (t, j) owns elements 8j .. 8j+7 (H/8 divides the workgroup size), so
-// the first log2(64) tree levels are xor-shuffles and the rest go through
-// LDS. Workgroup w computes expert w's logits.
+// the first log2(64) tree levels are lane exchanges and the rest go through
+// LDS. Workgroup w computes expert w's logits. inv_rms comes from the O
+// projection's per-tile partial sums of squares, requested together with the
+// router row and the first batch of h1.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void fill_x_pool_router(const Params& p, Smem& sm) {
   const int K = p.H, NT = p.NT, K8 = K / 8;
@@ -987,6 +1006,7 @@ __device__ __forceinline__ void fill_x_pool_router(const Params& p, Smem& sm) {
   const int nit = (kMaxTok + tstep - 1) / tstep;
   const int inwave = K8 < 64 ? K8 : 64;
   float* blk = &sm.red[0][0][0];  // [token][64-element block] sums when K8 > 64
+  const SsqLoads sq = ssq_issue(p, p.ssq1);
   float wv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (route) {
     const float4* wp = reinterpret_cast<const float4*>(p.cur.w_router + (size_t)e * K + j8 * 8);
@@ -1001,17 +1021,24 @@ __device__ __forceinline__ void fill_x_pool_router(const Params& p, Smem& sm) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) gv[j] = bf2f((uint16_t)(gw[j >> 1] >> ((j & 1) * 16)));
   }
-  for (int it0 = 0; it0 < nit; it0 += kFillBatch) {
-   float4 ha[kFillBatch], hb[kFillBatch];
+  constexpr int B = 2 * kFillBatch;  // tokens of h1 per round trip
+  float4 ha[B], hb[B];
+  auto load_batch = [&](int it0) {
 #pragma unroll
-   for (int q = 0; q < kFillBatch; ++q) {
-     const int t = min(threadIdx.x / K8 + (it0 + q) * tstep, NT - 1);
-     const float4* hp = reinterpret_cast<const float4*>(p.h1 + (size_t)t * K + j8 * 8);
-     ha[q] = hp[0];
-     hb[q] = hp[1];
-   }
+    for (int q = 0; q < B; ++q) {
+      const int t = min(threadIdx.x / K8 + (it0 + q) * tstep, NT - 1);
+      const float4* hp = reinterpret_cast<const float4*>(p.h1 + (size_t)t * K + j8 * 8);
+      ha[q] = hp[0];
+      hb[q] = hp[1];
+    }
+  };
+  load_batch(0);
+  ssq_finish(p, sq, sm);  // inv_rms of every token, from the partials requested first
+  __syncthreads();
+  for (int it0 = 0; it0 < nit; it0 += B) {
+   if (it0 > 0) load_batch(it0);
 #pragma unroll
-   for (int q = 0; q < kFillBatch; ++q) {
+   for (int q = 0; q < B; ++q) {
     const int it = it0 + q;
     if (it >= nit) break;
     const int t = threadIdx.x / K8 + it * tstep;
@@ -1108,7 +1135,31 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __builtin_popcountll(
 // selected set is every key above it plus the lowest-index ties, and the
 // selected entries are ranked in LDS. The routing tables are then built
 // without serial loops.
-__device__ __forceinline__ void routing(const Params& p, Smem& sm, bool write_out) {
+// The routing inputs of this thread: the logits of the wave's two tokens and
+// the tensor scales of expert threadIdx.x, requested before the pooled
+// activation fill so the round trips overlap.
+constexpr int kTokPerWave = kMaxTok / kWaves;
+struct RouteLoads {
+  float v[kTokPerWave][kMaxE / 64];
+  float ts_gu, ts_dn;
+};
+
+__device__ __forceinline__ RouteLoads routing_issue(const Params& p) {
+  RouteLoads L;
+  const int lane = lane_id(), w = wave_id(), E = p.E, NT = p.NT;
+#pragma unroll
+  for (int tt = 0; tt < kTokPerWave; ++tt) {
+    const int t = min(w + tt * kWaves, NT - 1);
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) L.v[tt][j] = p.logits[(size_t)t * E + min(lane + j * 64, E - 1)];
+  }
+  const int e = min((int)threadIdx.x, E - 1);
+  L.ts_gu = p.cur.e_ts[2 * e];
+  L.ts_dn = p.cur.e_ts[2 * e + 1];
+  return L;
+}
+
+__device__ __forceinline__ void routing(const Params& p, Smem& sm, bool write_out, const RouteLoads& in) {
   Route& rt = route_of(sm);
   const int lane = lane_id(), w = wave_id();
   const int E = p.E, K = p.topk, NT = p.NT;
@@ -1117,18 +1168,8 @@ __device__ __forceinline__ void routing(const Params& p, Smem& sm, bool write_ou
     rt.count[threadIdx.x] = 0;
     rt.pos[threadIdx.x] = -1;
   }
-  // both tokens' logits first (one round trip)
-  constexpr int TPW = kMaxTok / kWaves;  // tokens per wave
-  float v[TPW][kMaxE / 64];
-#pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    const int t = min(w + tt * kWaves, NT - 1);
-#pragma unroll
-    for (int j = 0; j < kMaxE / 64; ++j) {
-      const int e = lane + j * 64;
-      v[tt][j] = p.logits[(size_t)t * E + min(e, E - 1)];
-    }
-  }
+  constexpr int TPW = kTokPerWave;
+  const auto& v = in.v;
   __syncthreads();
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
@@ -1223,9 +1264,9 @@ __device__ __forceinline__ void routing(const Params& p, Smem& sm, bool write_ou
   __syncthreads();
   const int n_sel = rt.n_sel;
   for (int i = threadIdx.x; i < n_sel * kMaxTok; i += kThreads) (&rt.tokgate[0][0])[i] = 0.0f;
-  for (int j = threadIdx.x; j < n_sel; j += kThreads) {
-    rt.ts_gu[j] = p.cur.e_ts[2 * rt.sel[j]];
-    rt.ts_dn[j] = p.cur.e_ts[2 * rt.sel[j] + 1];
+  if (threadIdx.x < E && rt.pos[threadIdx.x] >= 0) {
+    rt.ts_gu[rt.pos[threadIdx.x]] = in.ts_gu;
+    rt.ts_dn[rt.pos[threadIdx.x]] = in.ts_dn;
   }
   __syncthreads();
   if (threadIdx.x < NT * K) {
@@ -1304,6 +1345,99 @@ __device__ __forceinline__ void g1_point(const Params& p, const Route& rt, int u
   is.scale = p.cur.e_gu_sc + r_all * (P / 16) + g_ * 2;
 }
 
+// GEMM1 with 16 steps per unit (P = 2048), the loop unrolled over one unit:
+// ring slot, step, A-operand offset and epilogue position are compile-time.
+// The block scales of a unit (16 rows x 128 B) are read once, with two
+// 16-byte loads per lane (lane group g: bytes g*32 .. g*32+31 of its row),
+// when the issue cursor enters the unit; a step takes its two bytes from
+// the lane that holds them (ds_bpermute). This replaces a 2-byte scale load
+// per step, which touched 16 cache lines for 8 bytes each.
+constexpr int kG1UnitSteps = 16;
+static_assert(kG1UnitSteps == 2 * kG1Ring, "the issue cursor enters the next unit at step 8");
+
+__device__ __forceinline__ void g1_unit_scales(const G1Issue& is, uint4 (&sc)[2]) {
+  const int g_ = lane_id() >> 4;
+  // is.scale points at the lane group's 2-byte offset g*2; the row starts g*2 earlier
+  const uint8_t* row = is.scale - g_ * 2;
+  sc[0] = *reinterpret_cast<const uint4*>(row + g_ * 32);
+  sc[1] = *reinterpret_cast<const uint4*>(row + g_ * 32 + 16);
+}
+
+template <int ST>
+__device__ __forceinline__ uint32_t g1_step_scale(const uint4 (&sc)[2]) {
+  // bytes ST*8 + 2g .. +1 of the lane's row: held by lane group ST/4, dword
+  // (ST%4)*2 + g/2 of its 32 bytes, half g%2
+  const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4;
+  constexpr int d0 = (ST & 3) * 2;
+  const uint32_t w0[8] = {sc[0].x, sc[0].y, sc[0].z, sc[0].w, sc[1].x, sc[1].y, sc[1].z, sc[1].w};
+  const int src = (r_ + 16 * (ST >> 2)) * 4;
+  const uint32_t x0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)w0[d0]);
+  const uint32_t x1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)w0[d0 + 1]);
+  const uint32_t x = (g_ >> 1) ? x1 : x0;
+  return (x >> ((g_ & 1) * 16)) & 0xFFFFu;
+}
+
+template <bool debug>
+__device__ __forceinline__ void gemm1_units16(const Params& p, Smem& sm, const Route& rt, int u0, int my_units,
+                                              int w) {
+  uint8_t* stage = sm.x + kG1StageOff;
+  const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4;
+  const int I = p.I, P = p.P, ntile = I / 8;
+  uint4 ring[kG1Ring];
+  G1Issue is{0, 0, nullptr, nullptr};
+  g1_point(p, rt, u0 + w, is);
+  uint4 scn[2], scc[2];
+  g1_unit_scales(is, scn);
+  ring_fence();
+#pragma unroll
+  for (int i = 0; i < kG1Ring; ++i) {
+    ring[i] = *reinterpret_cast<const uint4*>(is.code + i * 64);
+    ring_fence();
+  }
+  const uint8_t* abase = sm.x + r_ * x_stride(P) + g_ * 64;
+  for (int m = 0; m < my_units; ++m) {
+    scc[0] = scn[0];
+    scc[1] = scn[1];
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const int u = u0 + w + kWaves * m;
+    const int j = u / ntile, it = u - j * ntile;
+#define G1_STEP(ST)                                                                                   \
+    {                                                                                                 \
+      uint4 bw[4];                                                                                    \
+      fp4_decode(ring[(ST) & (kG1Ring - 1)], g1_step_scale<(ST)>(scc), bw);                          \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                   \
+        acc = mfma_f16(*reinterpret_cast<const uint4*>(abase + (ST) * 256 + q * 16), bw[q], acc);    \
+      if constexpr (debug) {                                                                          \
+        if (p.dbg.dq_gu && rt.sel[j] == p.dbg.dq_expert) {                                            \
+          const int row = r_ < 8 ? it * 8 + r_ : I + it * 8 + (r_ - 8);                               \
+          uint4* dst = reinterpret_cast<uint4*>(p.dbg.dq_gu + (size_t)row * P + (ST) * 128 + g_ * 32); \
+          _Pragma("unroll") for (int q = 0; q < 4; ++q) dst[q] = bw[q];                               \
+        }                                                                                             \
+      }                                                                                               \
+      if ((ST) == kG1Ring && m + 1 < my_units) g1_point(p, rt, u + kWaves, is);                       \
+      if ((ST) == kG1Ring) g1_unit_scales(is, scn);                                                   \
+      ring[(ST) & (kG1Ring - 1)] = *reinterpret_cast<const uint4*>(is.code + (((ST) + kG1Ring) & 15) * 64); \
+      ring_fence();                                                                                   \
+    }
+    G1_STEP(0) G1_STEP(1) G1_STEP(2) G1_STEP(3) G1_STEP(4) G1_STEP(5) G1_STEP(6) G1_STEP(7)
+    G1_STEP(8) G1_STEP(9) G1_STEP(10) G1_STEP(11) G1_STEP(12) G1_STEP(13) G1_STEP(14) G1_STEP(15)
+#undef G1_STEP
+    // acc[q] = D[token 4g+q][column r]: gate (r < 8) or up (r >= 8) of i-row it*8 + (r & 7).
+    const float ts = rt.ts_gu[j];
+    uint16_t* srow = reinterpret_cast<uint16_t*>(stage + (size_t)(u - u0) * 256);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float up = __shfl_xor(acc[q], 8);
+      const int tok = 4 * g_ + q;
+      if (r_ < 8) {
+        const float gate = acc[q] * ts;
+        const float a = gate / (1.0f + expf(-gate)) * (up * ts);
+        srow[tok * 8 + r_] = f2h(a * rt.tokgate[j][tok]);
+      }
+    }
+  }
+}
+
 template <bool debug>
 __device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
   Route& rt = route_of(sm);
@@ -1316,7 +1450,9 @@ __device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
   const int u1 = (int)((long long)(blockIdx.x + 1) * U / gridDim.x);
   const int my_units = (u1 - u0 - w + kWaves - 1) / kWaves;  // units u0 + w + 8*m < u1
   const int total = my_units > 0 ? my_units * nsteps : 0;
-  if (total > 0) {
+  if (total > 0 && nsteps == kG1UnitSteps) {
+    gemm1_units16<debug>(p, sm, rt, u0, my_units, w);
+  } else if (total > 0) {
     G1Step ring[kG1Ring];
     G1Issue is{0, 0, nullptr, nullptr};
     g1_point(p, rt, u0 + w, is);
@@ -1670,7 +1806,6 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
 
   // router + pooler (both read n2 = RMSNorm(h1))
   {
-    compute_inv_rms(p, p.h1, p.ssq1, sm);
     fill_x_pool_router(p, sm);
     mark(kTrPoolFill);
     if (DEBUG && p.dbg.n2 && blockIdx.x == 0) dump_n2(p, sm);
@@ -1683,8 +1818,11 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   mark(kTrRouterPoolBar);
 
   // routing (every workgroup) + experts' gate/up
-  fill_x_sum(p.ppart, p.p_slices, p.P, p.NT, sm);
-  routing(p, sm, blockIdx.x == 0);
+  {
+    const RouteLoads rl = routing_issue(p);
+    fill_x_sum(p.ppart, p.p_slices, p.P, p.NT, sm);
+    routing(p, sm, blockIdx.x == 0, rl);
+  }
   mark(kTrRouting);
   if (DEBUG && blockIdx.x == 0) {
     if (p.dbg.logits)
