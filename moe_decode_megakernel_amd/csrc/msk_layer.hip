@@ -176,8 +176,8 @@ __device__ __forceinline__ float lane_tree_sum(float acc, int n) {
 // start clean at the launch boundary). Arriving: every wave waits for its
 // stores to complete (s_waitcnt vmcnt(0)), the workgroup meets, and one
 // thread publishes the barrier's sequence number in the workgroup's own flag
-// word (write-through). Waiting: thread i polls workgroup i's flag until it
-// reaches the sequence number (bounded spin), then the workgroup meets again.
+// word (write-through). Waiting: wave 0 polls all flags until each reaches
+// the sequence number (bounded spin), then the workgroup meets again.
 // Flags are packed 16 per 64-byte line. No atomics, no L2 writeback or
 // invalidate. Sequence numbers grow through a call (reset at its start).
 // ---------------------------------------------------------------------------
@@ -195,27 +195,47 @@ __device__ __forceinline__ void bar_arrive(Barrier& b) {
 }
 
 // Returns false if the launch must stop (timeout or an error raised elsewhere).
+// Wave 0 alone polls every workgroup's flag (4 per lane), so the other waves
+// may have weight loads in flight without delaying the polls (vector-memory
+// counts complete in order within a wave).
 __device__ __forceinline__ bool bar_wait(Barrier& b, Smem& sm) {
-  if (threadIdx.x == 0) sm.flag = 1;
-  __syncthreads();
-  if (threadIdx.x < gridDim.x) {
+  if (__builtin_amdgcn_readfirstlane(wave_id()) == 0) {
+    const int lane = lane_id(), G = gridDim.x;
+    int ok = 1;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    uint32_t polls = 0;
-    while (__hip_atomic_load(&b.flags[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < b.seq) {
-      if ((++polls & 63u) == 0) {
-        if (__hip_atomic_load(b.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { sm.flag = 0; break; }
+    for (uint32_t polls = 1;; ++polls) {
+      bool done = true;
+#pragma unroll
+      for (int j = 0; j < kMaxGrid / 64; ++j) {
+        const int i = min(lane + 64 * j, G - 1);
+        done = done && __hip_atomic_load(&b.flags[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= b.seq;
+      }
+      if (__ballot(!done) == 0) break;
+      if ((polls & 63u) == 0) {
+        if (__hip_atomic_load(b.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { ok = 0; break; }
         if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
-          __hip_atomic_store(b.err, kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          sm.flag = 0;
+          if (lane == 0) __hip_atomic_store(b.err, kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = 0;
           break;
         }
       }
     }
+    if (lane == 0) sm.flag = ok;
   }
   __syncthreads();
   const bool ok = sm.flag != 0;
   b.seq += 1;
-  __syncthreads();
+  return ok;
+}
+
+// bar_wait, with the next phase's weight prefetch issued by waves 1..7
+// before the wait and by wave 0 (the poller) after it.
+template <class F>
+__device__ __forceinline__ bool bar_wait_prefetch(Barrier& b, Smem& sm, F&& prefetch) {
+  const bool poller = __builtin_amdgcn_readfirstlane(wave_id()) == 0;
+  if (!poller) prefetch();
+  const bool ok = bar_wait(b, sm);
+  if (poller && ok) prefetch();
   return ok;
 }
 
@@ -1784,8 +1804,8 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   merge_phase<DEBUG>(p, p.cur);
   mark(kTrMerge);
   bar_arrive(bar);
-  dense_prefetch<Epi::OProj>(p, kSchOproj, p.cur.w_o, Dq, p.h_in, sm, ring);
-  if (!bar_wait(bar, sm)) return;
+  if (!bar_wait_prefetch(bar, sm, [&] { dense_prefetch<Epi::OProj>(p, kSchOproj, p.cur.w_o, Dq, p.h_in, sm, ring); }))
+    return;
   mark(kTrMergeBar);
 
   // output projection + residual
@@ -1797,8 +1817,8 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   }
   mark(kTrOproj);
   bar_arrive(bar);
-  dense_prefetch<Epi::Pool>(p, kSchPool, p.cur.w_pool, p.H, nullptr, sm, ring);
-  if (!bar_wait(bar, sm)) return;
+  if (!bar_wait_prefetch(bar, sm, [&] { dense_prefetch<Epi::Pool>(p, kSchPool, p.cur.w_pool, p.H, nullptr, sm, ring); }))
+    return;
   mark(kTrOprojBar);
   if (DEBUG && p.dbg.h1) {
     for (int i = blockIdx.x * kThreads + threadIdx.x; i < p.NT * p.H; i += gridDim.x * kThreads) p.dbg.h1[i] = p.h1[i];
@@ -1843,8 +1863,8 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   gemm2_phase<DEBUG>(p, sm);
   mark(kTrGemm2);
   bar_arrive(bar);
-  dense_prefetch<Epi::Unpool>(p, kSchUnpool, p.cur.w_unpool, p.P, p.h1, sm, ring);
-  if (!bar_wait(bar, sm)) return;
+  if (!bar_wait_prefetch(bar, sm, [&] { dense_prefetch<Epi::Unpool>(p, kSchUnpool, p.cur.w_unpool, p.P, p.h1, sm, ring); }))
+    return;
   mark(kTrGemm2Bar);
 
   // unpooler + residual
@@ -1866,8 +1886,8 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   mark(kTrUnpool);
   if constexpr ((MODE & kModeQkvNext) != 0) {
     bar_arrive(bar);
-    dense_prefetch<Epi::Qkv>(p, kSchQkv, p.nxt.w_qkv, p.H, nullptr, sm, ring);
-    if (!bar_wait(bar, sm)) return;
+    if (!bar_wait_prefetch(bar, sm, [&] { dense_prefetch<Epi::Qkv>(p, kSchQkv, p.nxt.w_qkv, p.H, nullptr, sm, ring); }))
+      return;
     mark(kTrUnpoolBar);
     fill_x_qkv(p, p.h_out, p.nxt.g_attn, p.ssq2, sm);
     mark(kTrQkvFill);
