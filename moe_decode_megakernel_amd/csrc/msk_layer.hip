@@ -954,9 +954,13 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
 
 // Merge of the split partials (log-sum-exp in base 2). One wave per
 // (token, q head, 32 dims): lane l takes dim d0 + (l & 31) of the splits
-// s = (l >> 5) + 2i, and lane s < S also holds split s's (m, l). Every
-// partial is requested at once; the per-split factors 2^(m_s - M) reach the
-// lanes by read-lane, and the two half-waves' sums meet in one exchange.
+// s = (l >> 5) + 2i, and lane s < S also holds split s's (m, l). The (m, l)
+// words and the first kMergeChunk partials per lane are requested together;
+// further splits (S > 2 * kMergeChunk) follow in a rolled loop. The split
+// factors 2^(m_s - M) reach the lanes by lane exchange, and the two
+// half-waves' sums meet in one exchange.
+constexpr int kMergeChunk = 16;
+
 template <bool debug>
 __device__ __forceinline__ void merge_phase(const Params& p, const LayerW& lw) {
   const int D = p.d, Dq = p.nq * D, group = p.nq / p.nkv;
@@ -973,25 +977,27 @@ __device__ __forceinline__ void merge_phase(const Params& p, const LayerW& lw) {
     const int base = attn_item_base(p, lw, r, g, gridDim.x, S);
     const int dim = dq * 32 + (lane & 31);
     const int nper = (S + 1) / 2;  // splits per half-wave (the odd half may have one fewer)
-    float ov[kMaxSplits / 2];
+    float2 ml = *reinterpret_cast<const float2*>(apart_at(p, base + min(lane, S - 1), w, t) + D);
+    float ov[kMergeChunk];
 #pragma unroll
-    for (int i = 0; i < kMaxSplits / 2; ++i) {
-      if (i < nper) ov[i] = apart_at(p, base + min(half + 2 * i, S - 1), w, t)[dim];
-    }
-    float2 ml = make_float2(-INFINITY, 0.0f);
-    if (lane < S) ml = *reinterpret_cast<const float2*>(apart_at(p, base + lane, w, t) + D);
+    for (int i = 0; i < kMergeChunk; ++i) ov[i] = apart_at(p, base + min(half + 2 * i, S - 1), w, t)[dim];
+    if (lane >= S) ml = make_float2(-INFINITY, 0.0f);
     float M = ml.x;
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     const float f = (ml.x == -INFINITY) ? 0.0f : exp2f(ml.x - M);
     float L = ml.y * f;
     for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
     float O = 0.0f;
+    for (int i0 = 0; i0 < nper; i0 += kMergeChunk) {
+      if (i0 > 0) {
 #pragma unroll
-    for (int i = 0; i < kMaxSplits / 2; ++i) {
-      if (i < nper) {
-        const float fe = readlane_f32(f, 2 * i), fo = readlane_f32(f, min(2 * i + 1, kMaxSplits - 1));
-        const bool valid = half + 2 * i < S;
-        O = fmaf(ov[i], valid ? (half ? fo : fe) : 0.0f, O);
+        for (int i = 0; i < kMergeChunk; ++i) ov[i] = apart_at(p, base + min(half + 2 * (i0 + i), S - 1), w, t)[dim];
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeChunk; ++i) {
+        const int sp = half + 2 * (i0 + i);
+        const float fs = __shfl(f, min(sp, 63));
+        O = fmaf(ov[i], sp < S ? fs : 0.0f, O);
       }
     }
     O += __shfl_xor(O, 32);
