@@ -35,7 +35,12 @@
  *  e_gate_up       [E][2I][P/2]  E2M1 codes, rows gate | up; element 2j of a
  *                                row in the low nibble of byte j
  *  e_gate_up_scale [E][2I][P/16] E4M3 (OCP, bias 7) scale per 16 elements
- *  e_down          [E][P][I/2]   E2M1;  e_down_scale [E][P][I/16] E4M3
+ *  e_down          [E][P][I/2]   E2M1
+ *  e_down_scale    E4M3 scale per 16 elements of e_down, tiled (written by
+ *                  msk_pack_down_scale from the row-major [E][P][I/16]):
+ *                  [E][P/16][S][16][8], S = ceil(I/128); byte b of row r in
+ *                  slice s of tile t scales elements 16*(8s+b) .. +15 of row
+ *                  16t+r; positions past I/16 hold 0
  *  e_tensor_scale  fp32 [E][2]   per-tensor scale of gate_up and of down
  *  k_cache, v_cache bf16 [max_requests][nkv][kv_capacity][d]
  * Activations: h_in / h_out fp32 [n_requests * n_tokens][H], request-major.
@@ -191,8 +196,25 @@ msk_status msk_verify_step(msk_handle h, const msk_io* io, void* stream);
 /* Release the handle (the workspace stays the caller's). */
 msk_status msk_destroy(msk_handle h);
 
-/* Description of the last error on h (or of the last msk_create failure when
- * h is NULL). Never NULL. */
+/* Bytes of a tiled e_down_scale buffer (see Weight layouts); 0 if the shape
+ * is invalid (n_experts > 0, pool_dim a multiple of 16, expert_inter a
+ * multiple of 32). */
+size_t msk_down_scale_bytes(int32_t n_experts, int32_t pool_dim, int32_t expert_inter);
+
+/* Reorder the down projection's block scales from row-major [E][P][I/16]
+ * (src) into the tiled order msk_load_layer takes (dst, msk_down_scale_bytes
+ * bytes). GEMM2 of the experts (the down projection, "NVFP4 expert SwiGLU" of
+ * the pages above) reduces over I in 128-element slices per wave and 16 rows
+ * of P per tile; in this order one wave's scales for one expert are one
+ * 128-byte line. Both buffers are the caller's device memory, 16-byte
+ * aligned, not overlapping. Asynchronous on `stream`; the values are not
+ * changed. Failures are reported through msk_last_error(NULL). */
+msk_status msk_pack_down_scale(const void* src, void* dst, int32_t n_experts, int32_t pool_dim,
+                               int32_t expert_inter, void* stream);
+
+/* Description of the last error on h (or, when h is NULL, of the last
+ * failure of a call made without a handle: msk_create, msk_pack_down_scale).
+ * Never NULL. */
 const char* msk_last_error(msk_handle h);
 
 #ifdef __cplusplus

@@ -523,6 +523,23 @@ extern "C" msk_status msk_destroy(msk_handle h) {
   return MSK_OK;
 }
 
+extern "C" size_t msk_down_scale_bytes(int32_t n_experts, int32_t pool_dim, int32_t expert_inter) {
+  if (n_experts <= 0 || pool_dim <= 0 || pool_dim % 16 != 0 || expert_inter <= 0 || expert_inter % 32 != 0) return 0;
+  return (size_t)n_experts * pool_dim * msk::dn_scale_slices(expert_inter) * 8;
+}
+
+extern "C" msk_status msk_pack_down_scale(const void* src, void* dst, int32_t n_experts, int32_t pool_dim,
+                                          int32_t expert_inter, void* stream) {
+  if (!src || !dst) return fail(nullptr, MSK_E_INVALID, "src and dst are required");
+  if (!aligned16(src) || !aligned16(dst)) return fail(nullptr, MSK_E_ALIGN, "src and dst must be 16-byte aligned");
+  if (msk_down_scale_bytes(n_experts, pool_dim, expert_inter) == 0)
+    return fail(nullptr, MSK_E_SHAPE, "n_experts > 0, pool_dim a multiple of 16, expert_inter a multiple of 32 required");
+  const hipError_t e = msk_launch_pack_down_scale(static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), n_experts,
+                                                  pool_dim, expert_inter, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, MSK_E_HIP, std::string("scale packing launch failed: ") + hipGetErrorString(e));
+  return MSK_OK;
+}
+
 extern "C" const char* msk_last_error(msk_handle h) {
   if (!h) return g_create_error.c_str();
   return h->last_error.c_str();

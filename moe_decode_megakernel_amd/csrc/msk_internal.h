@@ -25,6 +25,11 @@ constexpr int kMaxQSlices = 4;             // split-K slices of the Q projection
 constexpr int kMaxSplits = 64;             // attention splits per (request, kv head)
 constexpr int kMaxPrefetch = 32;           // experts in a speculative prefetch list
 
+// k-slices of 128 elements per row of the down projection: its block scales
+// are stored tiled, [E][P/16][dn_scale_slices(I)][16 rows][8], so one wave's
+// scales for an (expert, 16-row tile, k-slice) are one 128-byte line.
+__host__ __device__ constexpr int dn_scale_slices(int I) { return (I + 127) / 128; }
+
 // Launch modes (bit set).
 enum : uint32_t {
   kModeQkvOwn = 1u,   // first phase: QKV projection + KV write of the launch's own layer
@@ -129,4 +134,5 @@ struct Params {
 
 // Launchers implemented in msk_layer.hip.
 hipError_t msk_launch_layer(const msk::Params& p, int grid, bool debug, hipStream_t s);
+hipError_t msk_launch_pack_down_scale(const uint8_t* src, uint8_t* dst, int E, int P, int I, hipStream_t s);
 hipError_t msk_launch_reset(uint32_t* bar, int32_t* err, hipStream_t s);

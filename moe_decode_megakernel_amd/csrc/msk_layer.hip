@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "msk_internal.h"
 
 namespace msk {
@@ -1584,7 +1586,10 @@ __device__ __forceinline__ void g2_issue(const Params& p, const Route& rt, int j
   const int kk = kv ? k : 0;
   const int row = tile * 16 + r_;
   b.c = *reinterpret_cast<const uint4*>(p.cur.e_dn + (size_t)e * P * (I / 2) + (size_t)row * (I / 2) + kk / 2);
-  b.s = *reinterpret_cast<const uint16_t*>(p.cur.e_dn_sc + (size_t)e * P * (I / 16) + (size_t)row * (I / 16) + kk / 16);
+  // tiled scales: this wave's 16 rows x 8 bytes of (e, tile) are one line
+  const int nsl = dn_scale_slices(I);
+  b.s = *reinterpret_cast<const uint16_t*>(p.cur.e_dn_sc + (((size_t)e * (P / 16) + tile) * nsl + min(w, nsl - 1)) * 128 +
+                                           r_ * 8 + g_ * 2);
   const bool routed = kv && r_ < p.NT && rt.tokgate[j][r_] != 0.0f;
   const uint16_t* src = routed ? p.abuf + ((size_t)j * p.NT + r_) * I + k : p.zeros;
   const int step = routed ? 8 : 0;
@@ -1705,7 +1710,7 @@ __device__ __forceinline__ void prefetch_rank(const Params& p, Smem& sm) {
 // down codes and scales; the workgroup is number `idx` of `n` prefetchers.
 __device__ __forceinline__ void prefetch_experts(const Params& p, const Smem& sm, int idx, int n) {
   const size_t I = p.I, P = p.P;
-  const size_t bytes[4] = {2 * I * P / 2, 2 * I * P / 16, P * I / 2, P * I / 16};
+  const size_t bytes[4] = {2 * I * P / 2, 2 * I * P / 16, P * I / 2, P * (size_t)dn_scale_slices(p.I) * 8};
   const uint8_t* base[4] = {p.cur.e_gu, p.cur.e_gu_sc, p.cur.e_dn, p.cur.e_dn_sc};
   int lines[4], lpe = 0;
 #pragma unroll
@@ -1934,6 +1939,35 @@ hipError_t msk_launch_layer(const msk::Params& p, int grid, bool debug, hipStrea
   }
   if (p.trace) return launch_mode<kTrace>(p, g, b, s);
   return launch_mode<kPlain>(p, g, b, s);
+}
+
+// Reorders the down projection's E4M3 block scales from row-major
+// [E][P][I/16] to the tiled order GEMM2 reads, [E][P/16][S][16][8] with
+// S = ceil(I/128): for each expert and 16-row tile, the 8 scales of k-slice s
+// (128 elements) of the 16 rows are one 128-byte line. Scale positions past
+// I/16 are zero. One thread per 8-byte group.
+__global__ void pack_down_scale_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int E, int P, int I) {
+  const int S = msk::dn_scale_slices(I), cols = I / 16;
+  const size_t n = (size_t)E * (P / 16) * S * 16;
+  for (size_t g = blockIdx.x * (size_t)blockDim.x + threadIdx.x; g < n; g += (size_t)gridDim.x * blockDim.x) {
+    const int r = (int)(g & 15);
+    const size_t ts = g >> 4;                 // (expert, tile, slice)
+    const int s = (int)(ts % S);
+    const size_t row = (ts / S) * 16 + r;     // expert * P + tile * 16 + r
+    uint64_t v = 0;
+    for (int b = 0; b < 8; ++b) {
+      const int c = s * 8 + b;
+      if (c < cols) v |= (uint64_t)src[row * cols + c] << (8 * b);
+    }
+    reinterpret_cast<uint64_t*>(dst)[g] = v;
+  }
+}
+
+hipError_t msk_launch_pack_down_scale(const uint8_t* src, uint8_t* dst, int E, int P, int I, hipStream_t s) {
+  const size_t n = (size_t)E * (P / 16) * msk::dn_scale_slices(I) * 16;
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(pack_down_scale_kernel, dim3(blocks), dim3(256), 0, s, src, dst, E, P, I);
+  return hipGetLastError();
 }
 
 hipError_t msk_launch_reset(uint32_t* bar, int32_t* err, hipStream_t s) {

@@ -17,7 +17,8 @@ STATUS_NAMES = ["MSK_OK", "MSK_E_INVALID", "MSK_E_SHAPE", "MSK_E_ALIGN", "MSK_E_
 MSK_FLAG_NO_NORM = 0x1
 
 EXPORTS = ("msk_workspace_bytes", "msk_create", "msk_load_layer", "msk_verify_layer",
-           "msk_verify_step", "msk_destroy", "msk_last_error")
+           "msk_verify_step", "msk_destroy", "msk_down_scale_bytes", "msk_pack_down_scale",
+           "msk_last_error")
 
 
 class msk_config(ctypes.Structure):
@@ -78,6 +79,10 @@ def lib():
         L.msk_verify_step.restype = i32
         L.msk_destroy.argtypes = [vp]
         L.msk_destroy.restype = i32
+        L.msk_down_scale_bytes.argtypes = [i32, i32, i32]
+        L.msk_down_scale_bytes.restype = ctypes.c_size_t
+        L.msk_pack_down_scale.argtypes = [vp, vp, i32, i32, i32, vp]
+        L.msk_pack_down_scale.restype = i32
         L.msk_last_error.argtypes = [vp]
         L.msk_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -117,6 +122,15 @@ def msk_verify_step(h, io: msk_io, stream: int) -> int:
 
 def msk_destroy(h) -> int:
     return lib().msk_destroy(h)
+
+
+def msk_down_scale_bytes(n_experts: int, pool_dim: int, expert_inter: int) -> int:
+    return lib().msk_down_scale_bytes(n_experts, pool_dim, expert_inter)
+
+
+def msk_pack_down_scale(src_ptr: int, dst_ptr: int, n_experts: int, pool_dim: int, expert_inter: int,
+                        stream: int) -> int:
+    return lib().msk_pack_down_scale(vp(src_ptr), vp(dst_ptr), n_experts, pool_dim, expert_inter, vp(stream))
 
 
 def msk_last_error(h) -> str:
@@ -187,9 +201,30 @@ class Handle:
         if st != MSK_OK:
             raise MskError(st, msk_last_error(self.h))
 
+    def pack_down_scale(self, scale, stream=None):
+        """Tiled copy of a row-major [E][P][I/16] down-projection scale tensor
+        (the order msk_load_layer takes), written by msk_pack_down_scale on
+        the current stream."""
+        import torch
+        c = self.cfg
+        n = msk_down_scale_bytes(c.n_experts, c.pool_dim, c.expert_inter)
+        if n == 0:
+            raise MskError(MSK_E_SHAPE, "msk_down_scale_bytes rejected the shape")
+        out = torch.empty(n, dtype=torch.uint8, device=scale.device)
+        s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        st = msk_pack_down_scale(scale.data_ptr(), out.data_ptr(), c.n_experts, c.pool_dim, c.expert_inter, s)
+        if st != MSK_OK:
+            raise MskError(st, msk_last_error(None))
+        return out
+
     def load_layer(self, layer, tensors: Dict, window: int):
-        self.layers[layer] = tensors
-        self.check(msk_load_layer(self.h, layer, make_layer_desc(tensors, window)))
+        """Register a layer whose tensors use the row-major layouts (the
+        down-projection scales are packed here into a tensor the handle
+        keeps)."""
+        t = dict(tensors)
+        t["e_down_scale"] = self.pack_down_scale(tensors["e_down_scale"])
+        self.layers[layer] = t
+        self.check(msk_load_layer(self.h, layer, make_layer_desc(t, window)))
 
     def verify_layer(self, layer, io, stream=None):
         import torch

@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("msk_workspace_bytes", "msk_create", "msk_load_layer", "msk_verify_layer", "msk_verify_step",
-              "msk_destroy", "msk_last_error"):
+              "msk_destroy", "msk_down_scale_bytes", "msk_pack_down_scale", "msk_last_error"):
         assert n in names, n
 
 
@@ -58,6 +58,24 @@ def test_error_paths_without_a_device():
     bad = msk.make_config(w, max_tokens=32)
     assert msk.msk_workspace_bytes(bad) == 0
     assert msk.lib().msk_destroy(None) == msk.MSK_E_INVALID
+
+
+def test_down_scale_packing_checks_without_a_device():
+    """Size rule of the tiled down-projection scales, and the argument checks
+    msk_pack_down_scale makes before it launches anything."""
+    if not os.path.exists(LIB):
+        pytest.skip("libmsk.so not built")
+    from moe_decode_megakernel_amd import msk
+    # [E][P/16][ceil(I/128)][16][8] bytes
+    assert msk.msk_down_scale_bytes(256, 2048, 1024) == 256 * 2048 * 1024 // 16
+    assert msk.msk_down_scale_bytes(16, 128, 64) == 16 * 8 * 1 * 128
+    assert msk.msk_down_scale_bytes(4, 32, 160) == 4 * 2 * 2 * 128
+    for bad in ((0, 128, 64), (16, 100, 64), (16, 128, 48), (16, 128, 0)):
+        assert msk.msk_down_scale_bytes(*bad) == 0, bad
+    assert msk.msk_pack_down_scale(0, 4096, 16, 128, 64, 0) == msk.MSK_E_INVALID
+    assert "required" in msk.msk_last_error(None)
+    assert msk.msk_pack_down_scale(4104, 4096, 16, 128, 64, 0) == msk.MSK_E_ALIGN
+    assert msk.msk_pack_down_scale(4096, 8192, 16, 100, 64, 0) == msk.MSK_E_SHAPE
 
 
 @pytest.fixture(scope="module")
