@@ -41,8 +41,10 @@ constexpr int kUnitMaxK = msk::kSubK * msk::kWaves;  // one 128-k sub-unit per w
 // Longest-processing-time assignment of jobs to G workgroups. A splittable
 // tile becomes `slices` jobs of equal k ranges (partial slot = slice index);
 // an unsplit tile is one job. A job longer than one unit (kUnitMaxK) runs as
-// consecutive pieces on one workgroup, carrying the accumulator.
-SchedHost build_sched(const std::vector<TileSpec>& tiles, int slices, int G) {
+// consecutive pieces on one workgroup, carrying the accumulator. With
+// slice_groups, a job of slice s goes only to workgroups g with g mod slices
+// == s, so each workgroup's units lie in one k-slice.
+SchedHost build_sched(const std::vector<TileSpec>& tiles, int slices, int G, bool slice_groups = false) {
   struct Job {
     int tile, k0, klen, slot;
   };
@@ -59,8 +61,9 @@ SchedHost build_sched(const std::vector<TileSpec>& tiles, int slices, int G) {
   std::vector<std::vector<msk::Unit>> per(G);
   std::vector<int64_t> load(G, 0);
   for (const Job& j : jobs) {
-    int best = 0;
-    for (int g = 1; g < G; ++g)
+    const int g0 = slice_groups ? j.slot : 0, step = slice_groups ? slices : 1;
+    int best = g0;
+    for (int g = g0 + step; g < G; g += step)
       if (load[g] < load[best]) best = g;
     for (int k = 0; k < j.klen; k += kUnitMaxK) {
       int kl = std::min(kUnitMaxK, j.klen - k);
@@ -88,6 +91,28 @@ SchedHost build_sched_best(const std::vector<TileSpec>& tiles, int K, int G, int
   for (int s : {1, 2, 4}) {
     if (K % (s * msk::kSubK) != 0) continue;
     SchedHost sh = build_sched(tiles, s, G);
+    if (best.off.empty() || sh.max_load < best.max_load) {
+      best = std::move(sh);
+      best_s = s;
+    }
+  }
+  *slices_out = best_s;
+  return best;
+}
+
+// The pooler's schedule: slice count in {1, 2} (fewer slices among the
+// lowest max load) with each workgroup's units in slice g mod slices, so the
+// workgroup fills only that k-slice of its input. The router is split the
+// same way: slice s of expert e is pair e*slices + s, and workgroup g takes
+// pairs g, g+G, ...; a slice count is admitted when G is a multiple of it and
+// no workgroup gets more than kMaxRouterPerWg pairs.
+SchedHost build_sched_pool(const std::vector<TileSpec>& tiles, int K, int G, int E, int* slices_out) {
+  SchedHost best;
+  int best_s = 1;
+  for (int s : {1, 2}) {
+    if (K % (s * msk::kSubK) != 0 || G % s != 0) continue;
+    if ((E * s + G - 1) / G > msk::kMaxRouterPerWg) continue;
+    SchedHost sh = build_sched(tiles, s, G, true);
     if (best.off.empty() || sh.max_load < best.max_load) {
       best = std::move(sh);
       best_s = s;
@@ -184,7 +209,7 @@ Layout make_layout(const msk_config* c, int G) {
   L.qpart = take(4 * NT * Dq * 4);
   L.apart = take((size_t)G * msk::kWaves * msk::kMaxTok * (c->head_dim + 4) * 4);
   L.attn = take(NT * Dq * 2);
-  L.logits = take(NT * E * 4);
+  L.logits = take(4 * NT * E * 4);  // router partial sums per k-slice of the pooler
   L.ppart = take(4 * NT * P * 4);
   L.abuf = take(nsel * NT * I * 2);
   L.accpart = take(parts * NT * P * 4);
@@ -212,7 +237,8 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
   if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
     return fail(nullptr, MSK_E_HIP, "no HIP device");
   const int G = std::min(prop.multiProcessorCount, kMaxGrid);
-  if (cfg->n_experts > G) return fail(nullptr, MSK_E_SHAPE, "n_experts exceeds the workgroups of one launch (one router expert per workgroup)");
+  if (cfg->n_experts > msk::kMaxRouterPerWg * G)
+    return fail(nullptr, MSK_E_SHAPE, "n_experts exceeds the router rows the workgroups of one launch cover");
   {
     // GEMM1 stages 256 B per (selected expert, 8-row i-tile) unit of a workgroup in LDS
     const int64_t nsel = std::min<int64_t>(cfg->n_experts, (int64_t)pass_tokens(cfg) * cfg->top_k);
@@ -243,7 +269,11 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
   for (int t = 0; t < H / 16; ++t) t_unpool.push_back({t, P, false});
   SchedHost sq = build_sched_best(t_qkv, H, G, &h->q_slices);
   SchedHost so = build_sched(t_oproj, 1, G);
-  SchedHost sp = build_sched_best(t_pool, H, G, &h->p_slices);
+  SchedHost sp = build_sched_pool(t_pool, H, G, cfg->n_experts, &h->p_slices);
+  if (sp.off.empty()) {
+    delete h;
+    return fail(nullptr, MSK_E_SHAPE, "no pooler schedule fits this grid and expert count");
+  }
   SchedHost su = build_sched(t_unpool, 1, G);
 
   // per-workgroup tables: units [G][kSchCount][kMaxWgUnits], counts [G][kSchCount]

@@ -24,6 +24,7 @@ constexpr int kMaxWgUnits = 32;            // dense units of one workgroup in on
 constexpr int kMaxQSlices = 4;             // split-K slices of the Q projection
 constexpr int kMaxSplits = 64;             // attention splits per (request, kv head)
 constexpr int kMaxPrefetch = 32;           // experts in a speculative prefetch list
+constexpr int kMaxRouterPerWg = 2;         // router (expert, k-slice) pairs per workgroup
 
 // k-slices of 128 elements per row of the down projection: its block scales
 // are stored tiled, [E][P/16][dn_scale_slices(I)][16 rows][8], so one wave's
@@ -110,7 +111,7 @@ struct Params {
   float* qpart;           // [q_slices][NT][Dq]
   float* apart;           // attention partials
   uint16_t* attn;         // fp16 [NT][Dq] merged attention output
-  float* logits;          // [NT][E]
+  float* logits;          // [p_slices][NT][E] router subtree sums per k-slice (no bias)
   float* ppart;           // [p_slices][NT][P]
   uint16_t* abuf;         // f16 [n_sel_max][NT][I]
   float* accpart;         // [parts][NT][P]

@@ -206,13 +206,16 @@ __device__ __forceinline__ bool bar_wait(Barrier& b, Smem& sm) {
     int ok = 1;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     for (uint32_t polls = 1;; ++polls) {
-      bool done = true;
+      // all four flag loads in flight together, combined without a
+      // short-circuit (which would serialise them)
+      uint32_t f[kMaxGrid / 64];
 #pragma unroll
-      for (int j = 0; j < kMaxGrid / 64; ++j) {
-        const int i = min(lane + 64 * j, G - 1);
-        done = done && __hip_atomic_load(&b.flags[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= b.seq;
-      }
-      if (__ballot(!done) == 0) break;
+      for (int j = 0; j < kMaxGrid / 64; ++j)
+        f[j] = __hip_atomic_load(&b.flags[min(lane + 64 * j, G - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int behind = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxGrid / 64; ++j) behind += f[j] < b.seq ? 1 : 0;
+      if (__ballot(behind != 0) == 0) break;
       if ((polls & 63u) == 0) {
         if (__hip_atomic_load(b.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { ok = 0; break; }
         if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
@@ -1012,39 +1015,56 @@ __device__ __forceinline__ void merge_phase(const Params& p, const LayerW& lw) {
 }
 
 // ---------------------------------------------------------------------------
-// Pooler input and router, from one pass over h1. For every token t:
+// Pooler input and router, from one pass over this workgroup's k-slice of h1.
+// The pooler is split into S = p_slices equal k-slices and workgroup g's pool
+// units all lie in slice g mod S, so its MFMA operand is needed only there.
+// For every token t and k in the slice:
 //   n2[k] = fl32(fl32(h1[k] * inv_rms[t]) * g[k])      (the fp32 router input)
 //   X[t][k] = fp16(n2[k])                               (the pooler's MFMA operand)
-//   logit(t, e) = tree(partials) + b[e], with partial j the fma chain over
-//   k = 8j .. 8j+7 ascending and the partials combined pairwise, adjacent
-//   pairs first.
-// Thread (t, j) owns elements 8j .. 8j+7 (H/8 divides the workgroup size), so
-// the first log2(64) tree levels are lane exchanges and the rest go through
-// LDS. Workgroup w computes expert w's logits. inv_rms comes from the O
-// projection's per-tile partial sums of squares, requested together with the
-// router row and the first batch of h1.
+// A router logit is a pairwise tree over partials j (the fma chain over
+// k = 8j .. 8j+7, ascending), adjacent pairs first, plus the bias. A slice of
+// H/S elements is an aligned subtree, so the router is split the same way:
+// pair e*S + s is the subtree sum of expert e over slice s, workgroup g takes
+// pairs g, g+G, g+2G, ... (all in its own slice, as G is a multiple of S),
+// and routing adds the S subtree sums in tree order and then the bias.
+// Thread (t, j) owns elements 8j .. 8j+7 of the slice: the first log2(64)
+// tree levels are lane exchanges and the rest go through LDS. inv_rms comes
+// from the O projection's per-tile partial sums of squares, requested
+// together with the router rows and the first batch of h1.
 // ---------------------------------------------------------------------------
+// WIDE: the slice has at least 512 elements (K8 >= 64), so every wave holds
+// 64 consecutive partials of one token per step and the token index and tree
+// width are wave-uniform.
+template <bool WIDE>
 __device__ __forceinline__ void fill_x_pool_router(const Params& p, Smem& sm) {
-  const int K = p.H, NT = p.NT, K8 = K / 8;
+  const int S = p.p_slices, G = gridDim.x, NT = p.NT, E = p.E;
+  const int slice = (int)blockIdx.x % S;
+  const int Ks = p.H / S, k0 = slice * Ks, K8 = Ks / 8;
   const int lane = lane_id();
-  const int e = blockIdx.x;
-  const bool route = e < p.E;
   const int j8 = threadIdx.x % K8;
   const int tstep = kThreads / K8;
   const int nit = (kMaxTok + tstep - 1) / tstep;
-  const int inwave = K8 < 64 ? K8 : 64;
-  float* blk = &sm.red[0][0][0];  // [token][64-element block] sums when K8 > 64
+  const int inwave = WIDE ? 64 : (K8 < 64 ? K8 : 64);
+  const int t_base = WIDE ? __builtin_amdgcn_readfirstlane((int)threadIdx.x / K8) : (int)threadIdx.x / K8;
+  const int npairs = E * S;
+  const int n_re = (int)blockIdx.x < npairs ? (npairs - 1 - (int)blockIdx.x) / G + 1 : 0;
+  float* blk = &sm.red[0][0][0];  // [token][pair][64-element block] sums when K8 > 64
   const SsqLoads sq = ssq_issue(p, p.ssq1);
-  float wv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (route) {
-    const float4* wp = reinterpret_cast<const float4*>(p.cur.w_router + (size_t)e * K + j8 * 8);
+  float wv[kMaxRouterPerWg][8];
+  int ev[kMaxRouterPerWg];
+#pragma unroll
+  for (int m = 0; m < kMaxRouterPerWg; ++m) {
+    // rows past n_re repeat a valid row (unused), so every thread issues the
+    // same loads
+    ev[m] = min(((int)blockIdx.x + min(m, max(n_re - 1, 0)) * G) / S, E - 1);
+    const float4* wp = reinterpret_cast<const float4*>(p.cur.w_router + (size_t)ev[m] * p.H + k0 + j8 * 8);
     const float4 a = wp[0], b = wp[1];
-    wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w; wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
+    wv[m][0] = a.x; wv[m][1] = a.y; wv[m][2] = a.z; wv[m][3] = a.w;
+    wv[m][4] = b.x; wv[m][5] = b.y; wv[m][6] = b.z; wv[m][7] = b.w;
   }
-  const float bias = (route && p.cur.b_router) ? p.cur.b_router[e] : 0.0f;
   float gv[8];
   {
-    const uint4 gg = *reinterpret_cast<const uint4*>(p.cur.g_moe + j8 * 8);
+    const uint4 gg = *reinterpret_cast<const uint4*>(p.cur.g_moe + k0 + j8 * 8);
     const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) gv[j] = bf2f((uint16_t)(gw[j >> 1] >> ((j & 1) * 16)));
@@ -1054,8 +1074,8 @@ __device__ __forceinline__ void fill_x_pool_router(const Params& p, Smem& sm) {
   auto load_batch = [&](int it0) {
 #pragma unroll
     for (int q = 0; q < B; ++q) {
-      const int t = min(threadIdx.x / K8 + (it0 + q) * tstep, NT - 1);
-      const float4* hp = reinterpret_cast<const float4*>(p.h1 + (size_t)t * K + j8 * 8);
+      const int t = min(t_base + (it0 + q) * tstep, NT - 1);
+      const float4* hp = reinterpret_cast<const float4*>(p.h1 + (size_t)t * p.H + k0 + j8 * 8);
       ha[q] = hp[0];
       hb[q] = hp[1];
     }
@@ -1069,45 +1089,50 @@ __device__ __forceinline__ void fill_x_pool_router(const Params& p, Smem& sm) {
    for (int q = 0; q < B; ++q) {
     const int it = it0 + q;
     if (it >= nit) break;
-    const int t = threadIdx.x / K8 + it * tstep;
+    const int t = t_base + it * tstep;
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     uint4 out = make_uint4(0, 0, 0, 0);
-    float acc = 0.0f;
     if (t < NT) {
       const float4 a = ha[q], b = hb[q];
-      float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
       const float inv = sm.inv_rms[t];
       if (p.use_norm) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = (v[j] * inv) * gv[j];
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc = fmaf(v[j], wv[j], acc);
       out.x = pack2(f2h(v[0]), f2h(v[1]));
       out.y = pack2(f2h(v[2]), f2h(v[3]));
       out.z = pack2(f2h(v[4]), f2h(v[5]));
       out.w = pack2(f2h(v[6]), f2h(v[7]));
     }
-    if (t < kMaxTok) *reinterpret_cast<uint4*>(sm.x + t * x_stride(K) + j8 * 16) = out;
-    if (route) {
-      acc = lane_tree_sum(acc, inwave);
+    if (t < kMaxTok) *reinterpret_cast<uint4*>(sm.x + t * x_stride(p.H) + (k0 + j8 * 8) * 2) = out;
+#pragma unroll
+    for (int m = 0; m < kMaxRouterPerWg; ++m) {
+      if (m >= n_re) break;
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = fmaf(v[j], wv[m][j], acc);
+      acc = WIDE ? lane_tree_sum(acc, 64) : lane_tree_sum(acc, inwave);
       if (K8 <= 64) {
-        if (j8 == 0 && t < NT) st_wt(&p.logits[(size_t)t * p.E + e], acc + bias);
+        if (j8 == 0 && t < NT) st_wt(&p.logits[((size_t)slice * NT + t) * E + ev[m]], acc);
       } else if (lane == 0 && t < kMaxTok) {
-        blk[t * 8 + j8 / 64] = acc;
+        blk[(t * kMaxRouterPerWg + m) * 8 + j8 / 64] = acc;
       }
     }
    }
   }
-  if (route && K8 > 64) {
+  if (K8 > 64) {
     __syncthreads();
-    if (threadIdx.x < NT) {
-      const int nblk = K8 / 64;  // 2, 4 or 8
-      float v[8];
+    const int nblk = K8 / 64;  // 2, 4 or 8
+    for (int i = threadIdx.x; i < NT * n_re; i += kThreads) {
+      const int t = i / n_re, m = i - t * n_re;
+      float b[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = q < nblk ? blk[threadIdx.x * 8 + q] : 0.0f;
-      const float a0 = v[0] + v[1], a1 = v[2] + v[3], a2 = v[4] + v[5], a3 = v[6] + v[7];
+      for (int q = 0; q < 8; ++q) b[q] = q < nblk ? blk[(t * kMaxRouterPerWg + m) * 8 + q] : 0.0f;
+      const float a0 = b[0] + b[1], a1 = b[2] + b[3], a2 = b[4] + b[5], a3 = b[6] + b[7];
       const float r = nblk == 2 ? a0 : (nblk == 4 ? a0 + a1 : (a0 + a1) + (a2 + a3));
-      st_wt(&p.logits[(size_t)threadIdx.x * p.E + e], r + bias);
+      const int e = min(((int)blockIdx.x + m * G) / S, E - 1);
+      st_wt(&p.logits[((size_t)slice * NT + t) * E + e], r);
     }
   }
   vm_drain();
@@ -1167,29 +1192,47 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __builtin_popcountll(
 // the tensor scales of expert threadIdx.x, requested before the pooled
 // activation fill so the round trips overlap.
 constexpr int kTokPerWave = kMaxTok / kWaves;
+constexpr int kMaxPSlices = 2;  // pooler / router k-slices
+
 struct RouteLoads {
-  float v[kTokPerWave][kMaxE / 64];
+  float part[kTokPerWave][kMaxPSlices][kMaxE / 64];  // router subtree sums per k-slice
+  float bias[kMaxE / 64];
   float ts_gu, ts_dn;
 };
 
 __device__ __forceinline__ RouteLoads routing_issue(const Params& p) {
   RouteLoads L;
-  const int lane = lane_id(), w = wave_id(), E = p.E, NT = p.NT;
+  const int lane = lane_id(), w = wave_id(), E = p.E, NT = p.NT, S = p.p_slices;
 #pragma unroll
   for (int tt = 0; tt < kTokPerWave; ++tt) {
     const int t = min(w + tt * kWaves, NT - 1);
 #pragma unroll
-    for (int j = 0; j < kMaxE / 64; ++j) L.v[tt][j] = p.logits[(size_t)t * E + min(lane + j * 64, E - 1)];
+    for (int s = 0; s < kMaxPSlices; ++s)
+#pragma unroll
+      for (int j = 0; j < kMaxE / 64; ++j)
+        L.part[tt][s][j] = p.logits[((size_t)min(s, S - 1) * NT + t) * E + min(lane + j * 64, E - 1)];
   }
+  const float* b = p.cur.b_router;
+#pragma unroll
+  for (int j = 0; j < kMaxE / 64; ++j) L.bias[j] = b ? b[min(lane + j * 64, E - 1)] : 0.0f;
   const int e = min((int)threadIdx.x, E - 1);
   L.ts_gu = p.cur.e_ts[2 * e];
   L.ts_dn = p.cur.e_ts[2 * e + 1];
   return L;
 }
 
+// Logit = the router's k-slice subtree sums combined in tree order, + bias.
+__device__ __forceinline__ float route_logit(const RouteLoads& L, int S, int tt, int j) {
+  const float* q = L.part[tt][0] + j;
+  constexpr int J = kMaxE / 64;
+  const float r = S == 1 ? q[0] : q[0] + q[J];
+  return r + L.bias[j];
+}
+
+template <bool debug>
 __device__ __forceinline__ void routing(const Params& p, Smem& sm, bool write_out, const RouteLoads& in) {
   Route& rt = route_of(sm);
-  const int lane = lane_id(), w = wave_id();
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
   const int E = p.E, K = p.topk, NT = p.NT;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   if (threadIdx.x < kMaxE) {
@@ -1197,72 +1240,124 @@ __device__ __forceinline__ void routing(const Params& p, Smem& sm, bool write_ou
     rt.pos[threadIdx.x] = -1;
   }
   constexpr int TPW = kTokPerWave;
-  const auto& v = in.v;
+  float v[TPW][kMaxE / 64];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) v[tt][j] = route_logit(in, p.p_slices, tt, j);
+  if (debug && p.dbg.logits && write_out) {
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int t = w + tt * kWaves;
+#pragma unroll
+      for (int j = 0; j < kMaxE / 64; ++j)
+        if (t < NT && lane + j * 64 < E) p.dbg.logits[(size_t)t * E + lane + j * 64] = v[tt][j];
+    }
+  }
   __syncthreads();
+  // Threshold of each of the wave's tokens, bit by bit from the top, both
+  // tokens in one loop: T grows to the largest prefix value with at least K
+  // keys >= T. Once exactly K keys are >= T the selected set is fixed and that
+  // token stops (ties below T cannot enter).
+  uint32_t key[TPW][kMaxE / 64];
+  uint32_t Tt[TPW];
+  bool done[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const bool live = w + tt * kWaves < NT;
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) key[tt][j] = (live && lane + j * 64 < E) ? order_key(v[tt][j]) : 0u;
+    Tt[tt] = 0;
+    done[tt] = !live;
+  }
+#pragma unroll 4
+  for (int b = 31; b >= 0; --b) {
+    bool all = true;
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) all = all && done[tt];
+    if (all) break;
+    int cnt[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const uint32_t cand = Tt[tt] | (1u << b);
+      cnt[tt] = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxE / 64; ++j) cnt[tt] += popc64(__ballot(key[tt][j] >= cand));
+    }
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      if (!done[tt] && cnt[tt] >= K) {
+        Tt[tt] |= 1u << b;
+        done[tt] = cnt[tt] == K;
+      }
+    }
+  }
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int t = w + tt * kWaves;
     if (t >= NT) break;
-    uint32_t key[kMaxE / 64];
-#pragma unroll
-    for (int j = 0; j < kMaxE / 64; ++j) key[j] = (lane + j * 64 < E) ? order_key(v[tt][j]) : 0u;
-    uint32_t T = 0;
-    for (int b = 31; b >= 0; --b) {
-      const uint32_t cand = T | (1u << b);
-      int cnt = 0;
-#pragma unroll
-      for (int j = 0; j < kMaxE / 64; ++j) cnt += popc64(__ballot(key[j] >= cand));
-      if (cnt >= K) T = cand;
-    }
+    const uint32_t T = Tt[tt];
+    const uint32_t (&kk)[kMaxE / 64] = key[tt];
     int n_gt = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxE / 64; ++j) n_gt += popc64(__ballot(key[j] > T));
+    for (int j = 0; j < kMaxE / 64; ++j) n_gt += popc64(__ballot(kk[j] > T));
     int ties_before = 0;  // ties with a lower index (index = lane + 64*j)
     bool sel[kMaxE / 64];
 #pragma unroll
     for (int j = 0; j < kMaxE / 64; ++j) {
-      const uint64_t tie = __ballot(key[j] == T);
+      const uint64_t tie = __ballot(kk[j] == T);
       const int my_rank = ties_before + popc64(tie & lt_mask);
-      sel[j] = key[j] > T || (key[j] == T && my_rank < K - n_gt);
+      sel[j] = kk[j] > T || (kk[j] == T && my_rank < K - n_gt);
       ties_before += popc64(tie);
     }
-    // compact the k selected (index order) into per-wave LDS scratch
-    float* scr = &sm.red[0][w][0];  // [k] value, [k] index, as floats/bits
-    int base = 0;
+    // The K selected, in index order, moved to lanes 0..K-1 by forward lane
+    // permutes (unselected lanes write to lane 63, never read).
+    float mv = 0.0f;
+    int me = 0;
+    {
+      int base = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxE / 64; ++j) {
-      const uint64_t m = __ballot(sel[j]);
-      if (sel[j]) {
-        const int q = base + popc64(m & lt_mask);
-        scr[q] = v[tt][j];
-        scr[kMaxK + q] = __builtin_bit_cast(float, lane + j * 64);
+      for (int j = 0; j < kMaxE / 64; ++j) {
+        const uint64_t m = __ballot(sel[j]);
+        const int n = popc64(m);
+        const int dst = (sel[j] ? base + popc64(m & lt_mask) : 63) * 4;
+        const int pv = __builtin_amdgcn_ds_permute(dst, __builtin_bit_cast(int, v[tt][j]));
+        const int pe = __builtin_amdgcn_ds_permute(dst, lane + j * 64);
+        if (lane >= base && lane < base + n) {
+          mv = __builtin_bit_cast(float, pv);
+          me = pe;
+        }
+        base += n;
       }
-      base += popc64(m);
     }
-    __builtin_amdgcn_wave_barrier();
-    if (lane < K) {
-      const float mv = scr[lane];
-      const int me = __builtin_bit_cast(int, scr[kMaxK + lane]);
-      const uint32_t mk = order_key(mv);
-      int rank = 0;
-      float mx = mv;
-      for (int q = 0; q < K; ++q) {
-        const float ov = scr[q];
-        const int oe = __builtin_bit_cast(int, scr[kMaxK + q]);
+    // rank among the selected (value descending, index ascending) and the
+    // largest selected value, from read-lanes of lanes 0..K-1
+    const uint32_t mk = order_key(mv);
+    int rank = 0;
+    float mx = mv;
+#pragma unroll
+    for (int q = 0; q < kMaxK; ++q) {
+      if (q < K) {
+        const float ov = readlane_f32(mv, q);
+        const int oe = __builtin_amdgcn_readlane(me, q);
         const uint32_t ok = order_key(ov);
         rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
         mx = fmaxf(mx, ov);
       }
-      rt.ids[t][rank] = me;
-      scr[2 * kMaxK + rank] = expf(mv - mx);
     }
-    __builtin_amdgcn_wave_barrier();
+    // ids and softmax numerators to lane = rank; the sum in rank order
+    const float ev = expf(mv - mx);
+    const int rdst = (lane < K ? rank : 63) * 4;
+    const int rid = __builtin_amdgcn_ds_permute(rdst, me);
+    const float re = __builtin_bit_cast(float, __builtin_amdgcn_ds_permute(rdst, __builtin_bit_cast(int, ev)));
+    float ssum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kMaxK; ++q)
+      if (q < K) ssum += readlane_f32(re, q);
     if (lane < K) {
-      float ssum = 0.0f;
-      for (int q = 0; q < K; ++q) ssum += scr[2 * kMaxK + q];  // rank order
-      rt.gates[t][lane] = scr[2 * kMaxK + lane] / ssum;
+      rt.ids[t][lane] = rid;
+      rt.gates[t][lane] = re / ssum;
     }
-    __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
   // histogram and membership
@@ -1837,7 +1932,8 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
 
   // router + pooler (both read n2 = RMSNorm(h1))
   {
-    fill_x_pool_router(p, sm);
+    if (p.H >= 512 * p.p_slices) fill_x_pool_router<true>(p, sm);
+    else fill_x_pool_router<false>(p, sm);
     mark(kTrPoolFill);
     if (DEBUG && p.dbg.n2 && blockIdx.x == 0) dump_n2(p, sm);
     EpiArgs ea{nullptr, nullptr, nullptr, p.ppart, nullptr, nullptr, nullptr};
@@ -1852,12 +1948,10 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   {
     const RouteLoads rl = routing_issue(p);
     fill_x_sum(p.ppart, p.p_slices, p.P, p.NT, sm);
-    routing(p, sm, blockIdx.x == 0, rl);
+    routing<DEBUG>(p, sm, blockIdx.x == 0, rl);
   }
   mark(kTrRouting);
   if (DEBUG && blockIdx.x == 0) {
-    if (p.dbg.logits)
-      for (int i = threadIdx.x; i < p.NT * p.E; i += kThreads) p.dbg.logits[i] = p.logits[i];
     if (p.dbg.p)
       for (int i = threadIdx.x; i < p.NT * p.P; i += kThreads) {
         float v = 0.0f;

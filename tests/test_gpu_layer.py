@@ -115,3 +115,38 @@ def test_working_size_layer_matches_oracle(name):
     _check_routing(w, g, o, name)
     n_sel = len(np.unique(o["ids"]))
     say(f"[{name}] distinct experts {n_sel}")
+
+
+@pytest.mark.parametrize("case", ["tied_bias", "duplicate_rows"])
+def test_routing_with_exact_ties(case):
+    """Top-8 of 256 where the k-th place falls inside a group of exactly equal
+    logits: zero router weights with a bias on a 0.5 grid (every token sees
+    the same heavily tied logits), or router rows duplicated in pairs (each
+    logit equals its partner's bit for bit). The kernel's ids must equal the
+    oracle's top-k of the kernel's own logits (value descending, lower expert
+    index first among equal values)."""
+    from dataclasses import replace
+    w = replace(synth.WORKLOADS["tiny_swa"], name=f"tiny_ties_{case}", E=256, k=8)
+    lw, k, v, h = _inputs(w)
+    rng = np.random.default_rng(5)
+    if case == "tied_bias":
+        lw["w_router"] = np.zeros_like(lw["w_router"])
+        lw["b_router"] = (np.round(rng.standard_normal(w.E) * 2.0) / 2.0).astype(np.float32)
+    else:
+        wr = lw["w_router"].copy()
+        wr[1::2] = wr[0::2]
+        lw["w_router"] = wr
+        lw["b_router"] = None
+    run = GpuLayerRun(w, lw, k, v, h)
+    g = run.run()
+    run.close()
+    lg = g["logits"]
+    n_tied = 0
+    for t in range(w.NT):
+        ids = orc.topk(lg[t], w.k)
+        kth = lg[t][ids[-1]]
+        n_tied += int(np.sum(lg[t] == kth) > 1)
+        assert np.array_equal(g["ids"][t], ids), (case, t, g["ids"][t], ids)
+        assert np.max(np.abs(g["gates"][t] - orc.gates(lg[t], g["ids"][t]))) < 1e-6
+    say(f"[ties-{case}] tokens whose k-th logit is tied: {n_tied}/{w.NT}")
+    assert n_tied > 0
