@@ -84,11 +84,13 @@ SchedHost build_sched(const std::vector<TileSpec>& tiles, int slices, int G, boo
   return sh;
 }
 
-// Best slice count in {1, 2, 4} (fewest slices among the lowest max load).
+// Best slice count in 1 .. msk::kMaxQSlices (fewest slices among the lowest
+// max load). Attention reads every slice of Q, so the bound keeps its loads
+// and registers small.
 SchedHost build_sched_best(const std::vector<TileSpec>& tiles, int K, int G, int* slices_out) {
   SchedHost best;
   int best_s = 1;
-  for (int s : {1, 2, 4}) {
+  for (int s = 1; s <= msk::kMaxQSlices; s *= 2) {
     if (K % (s * msk::kSubK) != 0) continue;
     SchedHost sh = build_sched(tiles, s, G);
     if (best.off.empty() || sh.max_load < best.max_load) {
@@ -206,7 +208,7 @@ Layout make_layout(const msk_config* c, int G) {
   L.ssq2 = take((H / 16) * NT * 4);
   L.hbuf0 = take(NT * H * 4);
   L.hbuf1 = take(NT * H * 4);
-  L.qpart = take(4 * NT * Dq * 4);
+  L.qpart = take(msk::kMaxQSlices * NT * Dq * 4);
   L.apart = take((size_t)G * msk::kWaves * msk::kMaxTok * (c->head_dim + 4) * 4);
   L.attn = take(NT * Dq * 2);
   L.logits = take(4 * NT * E * 4);  // router partial sums per k-slice of the pooler

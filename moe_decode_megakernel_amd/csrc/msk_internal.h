@@ -21,7 +21,7 @@ constexpr int kAttnChunk = 64;            // keys per attention chunk in LDS
 constexpr int kTraceSlots = 25;            // phase-boundary timestamps per workgroup per launch
 constexpr int kG1StageBytes = 32768;       // LDS staging of GEMM1 outputs per workgroup (256 B per unit)
 constexpr int kMaxWgUnits = 32;            // dense units of one workgroup in one schedule
-constexpr int kMaxQSlices = 4;             // split-K slices of the Q projection
+constexpr int kMaxQSlices = 2;             // split-K slices of the Q projection
 constexpr int kMaxSplits = 64;             // attention splits per (request, kv head)
 constexpr int kMaxPrefetch = 32;           // experts in a speculative prefetch list
 constexpr int kMaxRouterPerWg = 2;         // router (expert, k-slice) pairs per workgroup
