@@ -1660,8 +1660,8 @@ __device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
 // GEMM2: down projection, summed over a contiguous range of selected experts.
 // Workgroup = (row tile of 16 of P, expert part); wave w owns k in
 // [w*128, w*128+128) of I (lane group g: 32 elements at w*128 + g*32). The A
-// operand of a token not routed to the expert (or of k beyond I) is read from
-// a zero line in the workspace, so every expert issues the same loads. Per
+// operand of a token not routed to the expert (or of k beyond I) is zero
+// without a load; the weight loads are the same for every expert. Per
 // expert the fp32 tensor scale is applied to the MFMA partial before it is
 // added to the running sum.
 constexpr int kG2Ring = 4;  // GEMM2 experts whose loads are in flight per wave
@@ -1685,11 +1685,17 @@ __device__ __forceinline__ void g2_issue(const Params& p, const Route& rt, int j
   const int nsl = dn_scale_slices(I);
   b.s = *reinterpret_cast<const uint16_t*>(p.cur.e_dn_sc + (((size_t)e * (P / 16) + tile) * nsl + min(w, nsl - 1)) * 128 +
                                            r_ * 8 + g_ * 2);
+  // Only lanes of tokens routed to the expert load their A fragment; the
+  // rest are zero without a memory access.
   const bool routed = kv && r_ < p.NT && rt.tokgate[j][r_] != 0.0f;
-  const uint16_t* src = routed ? p.abuf + ((size_t)j * p.NT + r_) * I + k : p.zeros;
-  const int step = routed ? 8 : 0;
+  if (routed) {
+    const uint16_t* src = p.abuf + ((size_t)j * p.NT + r_) * I + k;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) b.a[q] = *reinterpret_cast<const uint4*>(src + q * step);
+    for (int q = 0; q < 4; ++q) b.a[q] = *reinterpret_cast<const uint4*>(src + q * 8);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b.a[q] = make_uint4(0, 0, 0, 0);
+  }
 }
 
 template <bool debug>
@@ -1888,22 +1894,27 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   }
   (void)Nqkv;
 
-  // attention of the launch's layer
-  if (p.d == 128) attention_phase<128>(p, p.cur, sm, trace_row);
-  else attention_phase<64>(p, p.cur, sm, trace_row);
-  if (p.n_prefetch > 0) {
-    const int n_items = attn_item_count(p, p.cur, gridDim.x);
-    const bool idle = (int)blockIdx.x >= n_items;
-    if (idle || (blockIdx.x == 0 && p.out_prefetch)) {
+  // attention of the launch's layer. Workgroups without an attention item
+  // publish nothing in this phase: with a speculative prefetch they arrive at
+  // the barrier first and read the listed experts while the others attend.
+  const int n_items = p.n_prefetch > 0 ? attn_item_count(p, p.cur, gridDim.x) : (int)gridDim.x;
+  if ((int)blockIdx.x >= n_items) {
+    bar_arrive(bar);
+    prefetch_rank(p, sm);
+    __syncthreads();
+    prefetch_experts(p, sm, blockIdx.x - n_items, gridDim.x - n_items);
+    mark(kTrAttn);
+  } else {
+    if (p.d == 128) attention_phase<128>(p, p.cur, sm, trace_row);
+    else attention_phase<64>(p, p.cur, sm, trace_row);
+    if (p.n_prefetch > 0 && blockIdx.x == 0 && p.out_prefetch) {
       prefetch_rank(p, sm);
       __syncthreads();
-      if (blockIdx.x == 0 && p.out_prefetch && threadIdx.x < p.n_prefetch)
-        p.out_prefetch[threadIdx.x] = sm.plist[threadIdx.x];
-      if (idle) prefetch_experts(p, sm, blockIdx.x - n_items, gridDim.x - n_items);
+      if (threadIdx.x < p.n_prefetch) p.out_prefetch[threadIdx.x] = sm.plist[threadIdx.x];
     }
+    mark(kTrAttn);
+    bar_arrive(bar);
   }
-  mark(kTrAttn);
-  bar_arrive(bar);
   if (!bar_wait(bar, sm)) return;
   mark(kTrAttnBar);
 
