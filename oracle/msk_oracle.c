@@ -232,27 +232,64 @@ static void linear_f64(const double* x, int32_t nt, const double* W, int32_t row
  * window W > 0, j > ctx + t - W (W keys including itself). Scores are
  * q.k / sqrt(d); softmax; weighted sum of V rows. Caches: [nkv][cap][d] bf16.
  */
+static uint32_t tree_anc(const uint16_t* tree, int32_t t) {
+  return tree ? (uint32_t)tree[t] : ((2u << t) - 1u);
+}
+
+static int32_t popcount16(uint32_t v) {
+  int32_t n = 0;
+  for (; v; v &= v - 1u) ++n;
+  return n;
+}
+
+int32_t orc_tree_valid(const uint16_t* tree, int32_t T) {
+  int32_t t, u;
+  if (T < 1 || T > 16) return 0;
+  if (!tree) return 1;
+  for (t = 0; t < T; ++t) {
+    uint32_t a = tree[t];
+    if (!(a >> t & 1u) || (a >> (t + 1)) != 0u) return 0;
+    for (u = 0; u < t; ++u)
+      if ((a >> u & 1u) && (tree[u] & ~a) != 0u) return 0;
+  }
+  return 1;
+}
+
+/* Attention of token t over its visible keys (orcarouter.ai, section "Dove si
+ * colloca il confine del kernel": sliding-window or global attention over the
+ * KV cache; the tree of verified tokens as in orc_tree_valid). Token t stands
+ * at position ctx + depth(t) on its own path. Visible keys, in ascending
+ * cache order: prior rows j < ctx with j > pos - window (all of them when
+ * window == 0), then new token u's row ctx + u for each ancestor u whose
+ * path position ctx + depth(u) is also inside the window. With no tree this
+ * is the causal chain: rows max(0, ctx + t - window + 1) .. ctx + t. */
 void orc_attention(const double* q, const uint16_t* k_cache, const uint16_t* v_cache,
                    int32_t nq, int32_t nkv, int32_t d, int32_t cap, int32_t T, int32_t ctx,
-                   int32_t window, double* out) {
+                   int32_t window, const uint16_t* tree, double* out) {
   int32_t group = nq / nkv;
   double scale = 1.0 / sqrt((double)d);
   int32_t th;
 #pragma omp parallel for schedule(dynamic)
   for (th = 0; th < T * nq; ++th) {
     int32_t t = th / nq, h = th % nq, g = h / group;
-    int32_t pos = ctx + t;
+    uint32_t anc = tree_anc(tree, t);
+    int32_t pos = ctx + popcount16(anc) - 1;
     int32_t lo = window > 0 ? (pos - window + 1 > 0 ? pos - window + 1 : 0) : 0;
-    int32_t n = pos - lo + 1, j, c;
+    int32_t n = 0, j, c, u;
     const double* qv = q + (int64_t)t * nq * d + (int64_t)h * d;
     const uint16_t* kb = k_cache + (int64_t)g * cap * d;
     const uint16_t* vb = v_cache + (int64_t)g * cap * d;
-    double* s = (double*)malloc(sizeof(double) * (size_t)n);
+    int32_t* rows = (int32_t*)malloc(sizeof(int32_t) * (size_t)(ctx + T));
+    double* s;
     double m = -INFINITY, l = 0.0;
     double* o = out + (int64_t)t * nq * d + (int64_t)h * d;
+    for (j = lo; j < ctx; ++j) rows[n++] = j;
+    for (u = 0; u < T; ++u)
+      if ((anc >> u & 1u) && ctx + popcount16(tree_anc(tree, u)) - 1 >= lo) rows[n++] = ctx + u;
+    s = (double*)malloc(sizeof(double) * (size_t)n);
     for (j = 0; j < n; ++j) {
       double dot = 0.0;
-      for (c = 0; c < d; ++c) dot += qv[c] * orc_bf16_value(kb[(int64_t)(lo + j) * d + c]);
+      for (c = 0; c < d; ++c) dot += qv[c] * orc_bf16_value(kb[(int64_t)rows[j] * d + c]);
       s[j] = dot * scale;
       m = fmax(m, s[j]);
     }
@@ -262,10 +299,11 @@ void orc_attention(const double* q, const uint16_t* k_cache, const uint16_t* v_c
     }
     for (c = 0; c < d; ++c) {
       double acc = 0.0;
-      for (j = 0; j < n; ++j) acc += s[j] * orc_bf16_value(vb[(int64_t)(lo + j) * d + c]);
+      for (j = 0; j < n; ++j) acc += s[j] * orc_bf16_value(vb[(int64_t)rows[j] * d + c]);
       o[c] = acc / l;
     }
     free(s);
+    free(rows);
   }
 }
 
@@ -291,8 +329,8 @@ void orc_attention(const double* q, const uint16_t* k_cache, const uint16_t* v_c
  * Caches are [R][nkv][cap][d] bf16. Returns 0, or -1 on bad arguments.
  */
 int32_t orc_layer_forward(const orc_layer* L, int32_t R, int32_t T, const int32_t* ctx,
-                          const double* h_in, uint16_t* k_cache, uint16_t* v_cache,
-                          double* h_out, orc_stages* st) {
+                          const uint16_t* tree, const double* h_in, uint16_t* k_cache,
+                          uint16_t* v_cache, double* h_out, orc_stages* st) {
   const int32_t H = L->hidden, nq = L->n_q_heads, nkv = L->n_kv_heads, d = L->head_dim;
   const int32_t E = L->n_experts, K = L->top_k, P = L->pool_dim, I = L->expert_inter;
   const int32_t Dq = nq * d, Dkv = nkv * d, Nqkv = Dq + 2 * Dkv, NT = R * T;
@@ -304,8 +342,10 @@ int32_t orc_layer_forward(const orc_layer* L, int32_t R, int32_t T, const int32_
   int32_t i, r, t, e, j;
 
   if (!L || R <= 0 || T <= 0 || nq % nkv != 0 || P % 16 != 0 || I % 16 != 0 || K > E) return -1;
-  for (r = 0; r < R; ++r)
+  for (r = 0; r < R; ++r) {
     if (ctx[r] < 0 || ctx[r] + T > cap) return -1;
+    if (!orc_tree_valid(tree ? tree + (int64_t)r * T : NULL, T)) return -1;
+  }
 
   n1 = (double*)malloc(sizeof(double) * (size_t)NT * H);
   qkv = (double*)malloc(sizeof(double) * (size_t)NT * Nqkv);
@@ -355,7 +395,7 @@ int32_t orc_layer_forward(const orc_layer* L, int32_t R, int32_t T, const int32_
   for (r = 0; r < R; ++r) {
     int64_t off = (int64_t)r * nkv * cap * d;
     orc_attention(q + (int64_t)r * T * Dq, k_cache + off, v_cache + off, nq, nkv, d, cap, T,
-                  ctx[r], L->window, attn + (int64_t)r * T * Dq);
+                  ctx[r], L->window, tree ? tree + (int64_t)r * T : NULL, attn + (int64_t)r * T * Dq);
   }
   if (st && st->attn) memcpy(st->attn, attn, sizeof(double) * (size_t)NT * Dq);
 

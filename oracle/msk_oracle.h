@@ -83,12 +83,21 @@ void orc_gates(const float* logits, const int32_t* ids, int32_t k, double* gates
 void orc_prefetch_list(const int32_t* ids, int32_t n_ids, int32_t n_experts, int32_t p, int32_t* list);
 void orc_rmsnorm(const double* x, const uint16_t* g, int32_t n, double eps, double* y);
 double orc_silu(double x);
+/* Verify-token trees (orcarouter.ai, "Muse Spark Open: 1.109 token al
+ * secondo ...", section "Anche il modello draft e' diventato piu' veloce":
+ * the 16 verified tokens form a tree of candidates rather than a chain).
+ * tree[t] is the ancestor set of token t as a bitmask over the T new tokens,
+ * self included; NULL means the chain (bits 0..t). Valid masks hold bit t,
+ * no bit above t, and are closed (an ancestor's ancestors are ancestors);
+ * depth(t) = popcount(tree[t]) - 1 is the token's distance from the prior
+ * context. Returns 1 if valid. */
+int32_t orc_tree_valid(const uint16_t* tree, int32_t T);
 void orc_attention(const double* q, const uint16_t* k_cache, const uint16_t* v_cache,
                    int32_t nq, int32_t nkv, int32_t d, int32_t cap, int32_t T, int32_t ctx,
-                   int32_t window, double* out);
+                   int32_t window, const uint16_t* tree, double* out);
 int32_t orc_layer_forward(const orc_layer* L, int32_t R, int32_t T, const int32_t* ctx,
-                          const double* h_in, uint16_t* k_cache, uint16_t* v_cache,
-                          double* h_out, orc_stages* st);
+                          const uint16_t* tree, const double* h_in, uint16_t* k_cache,
+                          uint16_t* v_cache, double* h_out, orc_stages* st);
 int32_t orc_threads(void);
 void orc_dense_swiglu(const double* x, int32_t nt, const double* wgu, const double* wd,
                       int32_t P, int32_t I, double* y);

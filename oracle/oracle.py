@@ -59,9 +59,11 @@ def lib():
         L.orc_rmsnorm.argtypes = [vp, vp, c_i32, c_f64, vp]
         L.orc_silu.argtypes = [c_f64]
         L.orc_silu.restype = c_f64
-        L.orc_attention.argtypes = [vp, vp, vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, vp]
-        L.orc_layer_forward.argtypes = [ctypes.POINTER(OrcLayer), c_i32, c_i32, vp, vp, vp, vp, vp,
+        L.orc_attention.argtypes = [vp, vp, vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, vp, vp]
+        L.orc_layer_forward.argtypes = [ctypes.POINTER(OrcLayer), c_i32, c_i32, vp, vp, vp, vp, vp, vp,
                                         ctypes.POINTER(OrcStages)]
+        L.orc_tree_valid.argtypes = [vp, c_i32]
+        L.orc_tree_valid.restype = c_i32
         L.orc_layer_forward.restype = c_i32
         L.orc_dense_swiglu.argtypes = [vp, c_i32, vp, vp, c_i32, c_i32, vp]
         L.orc_threads.restype = c_i32
@@ -144,12 +146,29 @@ def silu(x: float) -> float:
     return lib().orc_silu(x)
 
 
-def attention(q, k_cache, v_cache, nq, nkv, d, cap, T, ctx, window):
-    """q: [T][nq*d] fp64; caches: [nkv][cap][d] bf16 of one request."""
+def _tree_arg(tree, n):
+    if tree is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(tree, np.uint16).reshape(-1))
+    if a.size != n:
+        raise ValueError(f"tree mask needs {n} entries")
+    return a
+
+
+def tree_valid(tree, T) -> bool:
+    """orc_tree_valid: self bit set, no later bit, closed under ancestry."""
+    a = _tree_arg(tree, T)
+    return bool(lib().orc_tree_valid(_p(a), T))
+
+
+def attention(q, k_cache, v_cache, nq, nkv, d, cap, T, ctx, window, tree=None):
+    """q: [T][nq*d] fp64; caches: [nkv][cap][d] bf16 of one request; tree: [T]
+    ancestor bitmasks of the verified tokens, or None for the chain."""
     q = np.ascontiguousarray(q, np.float64)
     out = np.empty((T, nq * d), np.float64)
+    tr = _tree_arg(tree, T)
     lib().orc_attention(_p(q), _p(np.ascontiguousarray(k_cache)), _p(np.ascontiguousarray(v_cache)),
-                        nq, nkv, d, cap, T, ctx, window, _p(out))
+                        nq, nkv, d, cap, T, ctx, window, _p(tr), _p(out))
     return out
 
 
@@ -165,7 +184,7 @@ def dense_swiglu(x, wgu, wd):
 
 
 def layer_forward(shape, w: dict, R: int, T: int, ctx, h_in, k_cache, v_cache, cap: int,
-                  eps: float = 1e-6, use_norm: bool = True, stages: bool = True):
+                  eps: float = 1e-6, use_norm: bool = True, stages: bool = True, tree=None):
     """One layer on the CPU. shape: object with H, nq, nkv, d, E, k, P, I.
     k_cache / v_cache ([R][nkv][cap][d] uint16) are updated in place (KV write).
     Returns (h_out fp64 [R*T][H], stages dict or None)."""
@@ -197,7 +216,8 @@ def layer_forward(shape, w: dict, R: int, T: int, ctx, h_in, k_cache, v_cache, c
         }
         stp = OrcStages(**{k: _p(v) for k, v in st.items()})
     assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
-    rc = lib().orc_layer_forward(ctypes.byref(L), R, T, _p(ctx_a), _p(h), _p(k_cache), _p(v_cache),
+    tr = _tree_arg(tree, R * T)
+    rc = lib().orc_layer_forward(ctypes.byref(L), R, T, _p(ctx_a), _p(tr), _p(h), _p(k_cache), _p(v_cache),
                                  _p(out), ctypes.byref(stp) if stp is not None else None)
     if rc != 0:
         raise ValueError("orc_layer_forward rejected its arguments")
