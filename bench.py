@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-layers", default="0,1,2,3,4,5,6,7", help="layers of the step the oracle times")
     ap.add_argument("--trace", action="store_true",
                     help="after timing, run one step with the self-timing kernel and print the phase breakdown")
+    ap.add_argument("--tree", action="store_true",
+                    help="verify a seeded random tree of candidate tokens per request instead of a chain")
     ap.add_argument("--graph", action="store_true",
                     help="capture each step's msk_verify_step in a HIP graph and time the replays")
     ap.add_argument("--expert-prefetch", type=int, default=None,
@@ -133,7 +135,8 @@ def main():
     ids = torch.zeros((nsteps, L, w.NT, w.k), dtype=torch.int32, device=dev)
     gates = torch.zeros((nsteps, L, w.NT, w.k), dtype=torch.float32, device=dev)
     ctx = [w.ctx] * w.R
-    ios = [msk.make_io(w.R, w.T, ctx, h_in[s], h_out, ids[s], gates[s]) for s in range(nsteps)]
+    trees = [synth.verify_tree(w.T, 1000 + r) for r in range(w.R)] if args.tree else None
+    ios = [msk.make_io(w.R, w.T, ctx, h_in[s], h_out, ids[s], gates[s], tree_mask=trees) for s in range(nsteps)]
 
     def eager(s):
         if w.n_layers == 1:
@@ -227,6 +230,7 @@ def main():
             "hidden": w.H, "heads": f"{w.nq}q/{w.nkv}kv x {w.d}", "experts": f"top-{w.k} of {w.E}",
             "pool": w.P, "expert_inter": w.I, "expert_format": "NVFP4 (E2M1 + E4M3/16 + fp32)",
             "dense_format": "bf16", "router": "fp32",
+            "verify": "tree (seeded random parents)" if args.tree else "chain",
         },
         "achieved_tbps": round(mean_bytes / (mean_ms * 1e-3) / 1e12, 3),
         "hbm_frac": round(mean_bytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

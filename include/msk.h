@@ -152,6 +152,18 @@ typedef struct {
                              100 MHz real-time counter, written by lane 0 of each
                              workgroup at the phase boundaries below; slots a launch
                              does not reach are left untouched. Exclusive with debug. */
+  const uint16_t* tree_mask; /* HOST, may be NULL (= the causal chain): [R][T] ancestor
+                             bitmasks of the verify tokens. The tokens of a request
+                             form a tree of candidates (orcarouter.ai, "Muse Spark
+                             Open: 1.109 token al secondo ...", section "Anche il
+                             modello draft e' diventato piu' veloce ..."). Bit u of
+                             token t's mask = t attends to new token u. Each mask
+                             must hold bit t, no bit above t, and the masks of its
+                             ancestors (MSK_E_INVALID otherwise). Token t's position
+                             is ctx_len + depth, depth = ancestors other than t: the
+                             window covers the last `window` tokens of its own
+                             sequence (prior context, then its path). K/V are still
+                             written at ctx_len + t. Read at enqueue time. */
 } msk_io;
 
 /* Trace slots, in execution order ("_BAR" = after the grid barrier that

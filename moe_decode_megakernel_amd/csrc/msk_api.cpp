@@ -384,6 +384,18 @@ msk_status check_io(msk_handle h, const msk_io* io) {
   if ((io->expert_ids && !aligned16(io->expert_ids)) || (io->gates && !aligned16(io->gates)))
     return fail(h, MSK_E_ALIGN, "expert_ids/gates must be 16-byte aligned");
   if (io->prefetch_ids && !aligned16(io->prefetch_ids)) return fail(h, MSK_E_ALIGN, "prefetch_ids must be 16-byte aligned");
+  if (io->tree_mask) {
+    const int T = io->n_tokens;
+    for (int r = 0; r < io->n_requests; ++r)
+      for (int t = 0; t < T; ++t) {
+        const uint32_t a = io->tree_mask[r * T + t];
+        if (!((a >> t) & 1u) || (a >> (t + 1)) != 0u)
+          return fail(h, MSK_E_INVALID, "tree_mask: a token's mask must hold itself and no later token");
+        for (int u = 0; u < t; ++u)
+          if (((a >> u) & 1u) && (io->tree_mask[r * T + u] & ~a) != 0u)
+            return fail(h, MSK_E_INVALID, "tree_mask: a token's mask must hold its ancestors' masks");
+      }
+  }
   if (*h->err_host != 0) {
     int e = *h->err_host;
     *h->err_host = 0;
@@ -497,6 +509,17 @@ msk_status run_call(msk_handle h, int l0, int l1, const msk_io* io, hipStream_t 
       p.R = nr;
       p.NT = nr * T;
       for (int r = 0; r < msk::kMaxReq; ++r) p.ctx[r] = r < nr ? io->ctx_len[r0 + r] : 0;
+      for (int r = 0; r < msk::kMaxReq; ++r) {
+        uint64_t dp = 0;
+        for (int t = 0; t < msk::kMaxTok; ++t) {
+          uint32_t a = 0;
+          if (r < nr && t < T) a = io->tree_mask ? io->tree_mask[(r0 + r) * T + t] : ((2u << t) - 1u);
+          p.tree[r][t] = (uint16_t)a;
+          const uint64_t depth = a ? (uint64_t)(__builtin_popcount(a) - 1) : 0u;
+          dp |= depth << (4 * t);
+        }
+        p.tree_depth[r] = dp;
+      }
       p.mode = (i == 0 ? msk::kModeQkvOwn : 0u) | (i + 1 < n ? msk::kModeQkvNext : 0u);
       p.layer = l;
       p.bar_base = base;

@@ -95,6 +95,8 @@ struct Params {
   int32_t use_norm;
   float eps;
   int32_t ctx[kMaxReq];
+  uint16_t tree[kMaxReq][kMaxTok];  // ancestor bitmask of each verify token (self included)
+  uint64_t tree_depth[kMaxReq];     // 4 bits per token: its number of ancestors
   int32_t q_slices, p_slices;
   uint32_t mode;
   int32_t layer;          // layer whose attention .. unpooler this launch runs

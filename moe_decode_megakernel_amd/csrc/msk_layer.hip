@@ -128,6 +128,24 @@ __device__ __forceinline__ int ctx_of(const Params& p, int r) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Verify-token tree of request r (wave-uniform) seen from token t (per lane):
+// t's ancestor bitmask, and the packed depths of all the request's tokens.
+// Selects over the kernel-argument tables keep the reads scalar.
+__device__ __forceinline__ uint32_t tree_anc_of(const Params& p, int r, int t) {
+  uint32_t a = 0;
+#pragma unroll
+  for (int rr = 0; rr < kMaxReq; ++rr)
+#pragma unroll
+    for (int u = 0; u < kMaxTok; ++u) a = (r == rr && t == u) ? (uint32_t)p.tree[rr][u] : a;
+  return a;
+}
+__device__ __forceinline__ uint64_t tree_depth_of(const Params& p, int r) {
+  uint64_t d = p.tree_depth[0];
+#pragma unroll
+  for (int rr = 1; rr < kMaxReq; ++rr) d = (r == rr) ? p.tree_depth[rr] : d;
+  return d;
+}
+
 // Phase-boundary slots of the self-timing trace (one uint64 per slot, per
 // workgroup, per launch; 100 MHz real-time counter).
 enum TraceSlot {
@@ -765,6 +783,10 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
   const int h = it.g * group + w;
   const int ctx = ctx_of(p, it.r);
   const int window = lw.window;
+  // this lane's token: ancestor set and position ctx + depth on its own path
+  const uint32_t tanc = tree_anc_of(p, it.r, min(r_, kMaxTok - 1));
+  const uint64_t tdepth = tree_depth_of(p, it.r);
+  const int tpos = ctx + (int)((tdepth >> (4 * min(r_, kMaxTok - 1))) & 15u);
   constexpr int KS = D / 32;     // MFMA steps over the head dim
   constexpr int DT = D / 16;     // d tiles of the PV product
   constexpr int RS = D + 8;               // K tile row stride (elements): Ks[key][d]
@@ -892,11 +914,15 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
         uint4 a = *reinterpret_cast<const uint4*>(Ks + (kt * 16 + r_) * RS + s * 32 + g_ * 8);
         s4 = mfma_f16(a, qb[s], s4);
       }
-      const int pos = ctx + r_;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int key = kb + kt * 16 + 4 * g_ + i;
-        bool vis = key < it.k_end && key <= pos && (window <= 0 || key > pos - window) && r_ < p.T;
+        // prior rows by the window from the token's path position; new rows
+        // of its ancestors whose path position is inside the window
+        const int u = key - ctx;
+        const int kpos = key < ctx ? key : ctx + (int)((tdepth >> (4 * (u & 15))) & 15u);
+        bool vis = key < it.k_end && r_ < p.T && (key < ctx || ((tanc >> (u & 15)) & 1u)) &&
+                   (window <= 0 || kpos > tpos - window);
         sc[kt][i] = vis ? s4[i] * scale_log2 : -INFINITY;
       }
     }

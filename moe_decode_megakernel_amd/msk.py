@@ -47,7 +47,8 @@ class msk_debug(ctypes.Structure):
 class msk_io(ctypes.Structure):
     _fields_ = [("n_requests", i32), ("n_tokens", i32), ("ctx_len", ctypes.POINTER(i32)),
                 ("h_in", vp), ("h_out", vp), ("expert_ids", vp), ("gates", vp),
-                ("debug", ctypes.POINTER(msk_debug)), ("prefetch_ids", vp), ("trace", vp)]
+                ("debug", ctypes.POINTER(msk_debug)), ("prefetch_ids", vp), ("trace", vp),
+                ("tree_mask", ctypes.POINTER(ctypes.c_uint16))]
 
 
 TRACE_SLOTS = ["start", "qkv_own", "qkv_own_bar", "attn_q", "attn_kv", "attn", "attn_bar", "merge", "merge_bar", "oproj_fill",
@@ -165,13 +166,21 @@ def make_layer_desc(t: Dict, window: int) -> msk_layer_desc:
 
 
 def make_io(n_requests, n_tokens, ctx: Sequence[int], h_in, h_out, expert_ids=None, gates=None,
-            debug: Optional[msk_debug] = None, trace=None, prefetch_ids=None):
+            debug: Optional[msk_debug] = None, trace=None, prefetch_ids=None, tree_mask=None):
+    """tree_mask: host array-like [n_requests][n_tokens] of ancestor bitmasks, or None."""
     ctx_arr = (i32 * len(ctx))(*ctx)
+    tree_arr = None
+    if tree_mask is not None:
+        flat = [int(x) for row in tree_mask for x in (row if hasattr(row, "__len__") else [row])]
+        if len(flat) != n_requests * n_tokens:
+            raise ValueError("tree_mask needs n_requests * n_tokens entries")
+        tree_arr = (ctypes.c_uint16 * len(flat))(*flat)
     io = msk_io(n_requests=n_requests, n_tokens=n_tokens, ctx_len=ctypes.cast(ctx_arr, ctypes.POINTER(i32)),
                 h_in=_ptr(h_in), h_out=_ptr(h_out), expert_ids=_ptr(expert_ids), gates=_ptr(gates),
                 debug=ctypes.pointer(debug) if debug is not None else None, prefetch_ids=_ptr(prefetch_ids),
-                trace=_ptr(trace))
-    io._keep = (ctx_arr, debug)
+                trace=_ptr(trace),
+                tree_mask=ctypes.cast(tree_arr, ctypes.POINTER(ctypes.c_uint16)) if tree_arr is not None else None)
+    io._keep = (ctx_arr, debug, tree_arr)
     return io
 
 

@@ -343,3 +343,15 @@ def algorithmic_bytes_per_layer(w: Workload, layer: int, n_sel: int) -> int:
     kv_read = w.R * rows * w.nkv * w.d * 2 * 2
     kv_write = w.R * w.T * w.nkv * w.d * 2 * 2
     return dense + n_sel * expert + kv_read + kv_write
+
+
+def verify_tree(T, seed):
+    """Seeded tree of T verify tokens: the parent of token t is drawn uniformly
+    from -1 (a root on the prior context) and 0 .. t-1. Returns the ancestor
+    bitmask of every token (self included), uint16 [T]."""
+    rng = np.random.default_rng(seed)
+    anc = []
+    for t in range(T):
+        par = int(rng.integers(-1, t)) if t > 0 else -1
+        anc.append((1 << t) | (anc[par] if par >= 0 else 0))
+    return np.array(anc, np.uint16)

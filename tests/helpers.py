@@ -60,10 +60,11 @@ class GpuLayerRun:
         self.ctx = [w.ctx] * w.R if ctx is None else list(ctx)
         self.dq_expert = dq_expert
 
-    def run(self, debug=True):
+    def run(self, debug=True, tree=None):
         torch = self.torch
         d = msk.make_debug(self.dbg, self.dq_expert) if debug else None
-        io = msk.make_io(self.w.R, self.w.T, self.ctx, self.h_in, self.h_out, self.ids, self.gates, d)
+        io = msk.make_io(self.w.R, self.w.T, self.ctx, self.h_in, self.h_out, self.ids, self.gates, d,
+                         tree_mask=tree)
         self.handle.verify_layer(0, io)
         torch.cuda.synchronize()
         out = {k: v.cpu().numpy() for k, v in self.dbg.items()}
@@ -78,11 +79,11 @@ class GpuLayerRun:
         self.handle.close()
 
 
-def oracle_layer(w, lw, k, v, h, use_norm=True, ctx=None):
+def oracle_layer(w, lw, k, v, h, use_norm=True, ctx=None, tree=None):
     ctx = [w.ctx] * w.R if ctx is None else list(ctx)
     kk, vv = k.copy(), v.copy()
     out, st = orc.layer_forward(w, lw, w.R, w.T, ctx, np.asarray(h, np.float64), kk, vv, w.cap,
-                                eps=w.eps, use_norm=use_norm)
+                                eps=w.eps, use_norm=use_norm, tree=tree)
     st["h_out"] = out
     st["k_cache"] = kk
     st["v_cache"] = vv
@@ -115,3 +116,8 @@ def routing_mismatches(gpu_ids, logits, k, thr):
         if any(lg[ids[r + 1]] - lg[ids[r]] > thr for r in range(k - 1)):
             bad.append(t)
     return bad
+
+
+def random_tree(T, seed):
+    """Seeded tree of T verify tokens (ancestor bitmasks, self included)."""
+    return synth.verify_tree(T, seed)
