@@ -83,6 +83,59 @@ double orc_e4m3_value(uint8_t code) {
  * first) of byte r*cols/2 + c/2, times the E4M3 scale of its 16-element block
  * along the row, times the per-tensor fp32 scale. The product of the first two
  * is exact; in fp64 so is the third. */
+uint8_t orc_e4m3_rne_sat(float x) {
+  double v = x, q, r;
+  int e;
+  if (!(v > 0.0)) return 0;          /* 0 (and the sign-less activation scales) */
+  if (v >= 448.0) return 0x7E;       /* saturate: 448 = 1.75 * 2^8 */
+  if (v < ldexp(1.0, -6)) {          /* subnormal steps of 2^-9 */
+    r = rint(v / ldexp(1.0, -9));
+    return (uint8_t)r;               /* r = 8 is the smallest normal, code 0x08 */
+  }
+  frexp(v, &e);                      /* v = f * 2^e, f in [0.5, 1): exponent e - 1 */
+  q = v / ldexp(1.0, e - 1 - 3);     /* [8, 16) */
+  r = rint(q);
+  if (r == 16.0) {
+    r = 8.0;
+    e += 1;
+  }
+  {
+    int code = ((e - 1 + 7) << 3) | ((int)r - 8);
+    return (uint8_t)(code > 0x7E ? 0x7E : code);
+  }
+}
+
+uint8_t orc_e2m1_rne_sat(float y) {
+  const uint8_t s = signbit(y) ? 8 : 0;
+  const double a = fabs((double)y);
+  uint8_t c;
+  /* representable 0, .5, 1, 1.5, 2, 3, 4, 6; a tie goes to the code whose
+     mantissa bit is 0 */
+  if (a <= 0.25) c = 0;
+  else if (a < 0.75) c = 1;
+  else if (a <= 1.25) c = 2;
+  else if (a < 1.75) c = 3;
+  else if (a <= 2.5) c = 4;
+  else if (a < 3.5) c = 5;
+  else if (a <= 5.0) c = 6;
+  else c = 7;
+  return (uint8_t)(s | c);
+}
+
+void orc_nvfp4_quant16(const float* x, uint8_t* codes, uint8_t* scale, float* deq) {
+  float amax = 0.0f, s32, s;
+  int i;
+  for (i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  s32 = amax / 6.0f;
+  *scale = orc_e4m3_rne_sat(s32);
+  s = (float)orc_e4m3_value(*scale);
+  for (i = 0; i < 16; ++i) {
+    const float y = s > 0.0f ? x[i] / s : 0.0f;
+    codes[i] = orc_e2m1_rne_sat(y);
+    deq[i] = (float)(orc_e2m1_value(codes[i]) * (double)s);
+  }
+}
+
 void orc_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, double s_tensor,
                        int64_t rows, int64_t cols, double* out) {
   int64_t r;
@@ -460,6 +513,18 @@ int32_t orc_layer_forward(const orc_layer* L, int32_t R, int32_t T, const int32_
           gu[n] = s;
         }
         for (n = 0; n < I; ++n) a[n] = orc_silu(gu[n]) * gu[I + n];
+        if (L->act_fp4) {
+          /* NVFP4 activations: blocks of 16 along I, each value first
+             rounded to fp32 (see orc_nvfp4_quant16) */
+          int32_t b0;
+          for (b0 = 0; b0 < I; b0 += 16) {
+            float xb[16], dq[16];
+            uint8_t cq[16], sq;
+            for (n = 0; n < 16; ++n) xb[n] = (float)a[b0 + n];
+            orc_nvfp4_quant16(xb, cq, &sq, dq);
+            for (n = 0; n < 16; ++n) a[b0 + n] = dq[n];
+          }
+        }
         for (n = 0; n < P; ++n) {
           double s = 0.0;
           for (c = 0; c < I; ++c) s += wd[(int64_t)n * I + c] * a[c];

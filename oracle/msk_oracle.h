@@ -41,6 +41,7 @@ typedef struct {
   int32_t kv_capacity;  /* rows per (request, kv head) in the caches */
   float rms_eps;
   int32_t use_norm;     /* 1: RMSNorm before attention and before the MoE */
+  int32_t act_fp4;      /* 1: SwiGLU outputs quantized to NVFP4 before the down projection */
   const uint16_t* w_qkv;      /* bf16 [nq*d + 2*nkv*d][H], rows Q | K | V */
   const uint16_t* w_o;        /* bf16 [H][nq*d] */
   const float* w_router;      /* fp32 [E][H] */
@@ -92,6 +93,17 @@ double orc_silu(double x);
  * depth(t) = popcount(tree[t]) - 1 is the token's distance from the prior
  * context. Returns 1 if valid. */
 int32_t orc_tree_valid(const uint16_t* tree, int32_t T);
+/* NVFP4 quantization of activations (orcarouter.ai, section "Dove si colloca
+ * il confine del kernel": after the first expert GEMM the activations travel
+ * as fp4). One block = 16 consecutive fp32 values along the expert's
+ * intermediate dim; every step below is one fp32 operation:
+ *   amax = max |x_i|;  s = E4M3(fl32(amax / 6))  (round to nearest even,
+ *   saturating at 448);  q_i = E2M1(fl32(x_i / s))  (nearest, ties to the
+ *   even code, saturating at +-6, sign kept; 0 when s = 0);
+ *   deq_i = E2M1(q_i) * s  (exact). */
+uint8_t orc_e4m3_rne_sat(float x);
+uint8_t orc_e2m1_rne_sat(float y);
+void orc_nvfp4_quant16(const float* x, uint8_t* codes, uint8_t* scale, float* deq);
 void orc_attention(const double* q, const uint16_t* k_cache, const uint16_t* v_cache,
                    int32_t nq, int32_t nkv, int32_t d, int32_t cap, int32_t T, int32_t ctx,
                    int32_t window, const uint16_t* tree, double* out);

@@ -24,6 +24,7 @@ class OrcLayer(ctypes.Structure):
         ("hidden", c_i32), ("n_q_heads", c_i32), ("n_kv_heads", c_i32), ("head_dim", c_i32),
         ("n_experts", c_i32), ("top_k", c_i32), ("pool_dim", c_i32), ("expert_inter", c_i32),
         ("window", c_i32), ("kv_capacity", c_i32), ("rms_eps", c_f32), ("use_norm", c_i32),
+        ("act_fp4", c_i32),
         ("w_qkv", vp), ("w_o", vp), ("w_router", vp), ("b_router", vp), ("w_pool", vp),
         ("w_unpool", vp), ("g_attn", vp), ("g_moe", vp), ("e_gate_up", vp),
         ("e_gate_up_scale", vp), ("e_down", vp), ("e_down_scale", vp), ("e_tensor_scale", vp),
@@ -62,6 +63,11 @@ def lib():
         L.orc_attention.argtypes = [vp, vp, vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, vp, vp]
         L.orc_layer_forward.argtypes = [ctypes.POINTER(OrcLayer), c_i32, c_i32, vp, vp, vp, vp, vp, vp,
                                         ctypes.POINTER(OrcStages)]
+        L.orc_e4m3_rne_sat.argtypes = [c_f32]
+        L.orc_e4m3_rne_sat.restype = ctypes.c_uint8
+        L.orc_e2m1_rne_sat.argtypes = [c_f32]
+        L.orc_e2m1_rne_sat.restype = ctypes.c_uint8
+        L.orc_nvfp4_quant16.argtypes = [vp, vp, vp, vp]
         L.orc_tree_valid.argtypes = [vp, c_i32]
         L.orc_tree_valid.restype = c_i32
         L.orc_layer_forward.restype = c_i32
@@ -155,6 +161,34 @@ def _tree_arg(tree, n):
     return a
 
 
+def e4m3_rne_sat(x: float) -> int:
+    return int(lib().orc_e4m3_rne_sat(float(x)))
+
+
+def e2m1_rne_sat(y: float) -> int:
+    return int(lib().orc_e2m1_rne_sat(float(y)))
+
+
+def nvfp4_quant16(x):
+    """16 fp32 values -> (codes uint8 [16], E4M3 scale code, dequantized fp32 [16])."""
+    x = np.ascontiguousarray(np.asarray(x, np.float32).reshape(16))
+    codes = np.empty(16, np.uint8)
+    sc = np.empty(1, np.uint8)
+    deq = np.empty(16, np.float32)
+    lib().orc_nvfp4_quant16(_p(x), _p(codes), _p(sc), _p(deq))
+    return codes, int(sc[0]), deq
+
+
+def nvfp4_quant_rows(x):
+    """[rows][n] fp32 (n a multiple of 16) -> dequantized fp32, block by block."""
+    x = np.asarray(x, np.float32)
+    out = np.empty_like(x)
+    for r in range(x.shape[0]):
+        for b in range(0, x.shape[1], 16):
+            out[r, b:b + 16] = nvfp4_quant16(x[r, b:b + 16])[2]
+    return out
+
+
 def tree_valid(tree, T) -> bool:
     """orc_tree_valid: self bit set, no later bit, closed under ancestry."""
     a = _tree_arg(tree, T)
@@ -184,7 +218,8 @@ def dense_swiglu(x, wgu, wd):
 
 
 def layer_forward(shape, w: dict, R: int, T: int, ctx, h_in, k_cache, v_cache, cap: int,
-                  eps: float = 1e-6, use_norm: bool = True, stages: bool = True, tree=None):
+                  eps: float = 1e-6, use_norm: bool = True, stages: bool = True, tree=None,
+                  act_fp4: bool = False):
     """One layer on the CPU. shape: object with H, nq, nkv, d, E, k, P, I.
     k_cache / v_cache ([R][nkv][cap][d] uint16) are updated in place (KV write).
     Returns (h_out fp64 [R*T][H], stages dict or None)."""
@@ -192,7 +227,7 @@ def layer_forward(shape, w: dict, R: int, T: int, ctx, h_in, k_cache, v_cache, c
     NT = R * T
     L = OrcLayer(hidden=s.H, n_q_heads=s.nq, n_kv_heads=s.nkv, head_dim=s.d, n_experts=s.E,
                  top_k=s.k, pool_dim=s.P, expert_inter=s.I, window=int(w["window"]),
-                 kv_capacity=cap, rms_eps=eps, use_norm=1 if use_norm else 0)
+                 kv_capacity=cap, rms_eps=eps, use_norm=1 if use_norm else 0, act_fp4=1 if act_fp4 else 0)
     keep = {}
     for name in ("w_qkv", "w_o", "w_router", "b_router", "w_pool", "w_unpool", "g_attn", "g_moe",
                  "e_gate_up", "e_gate_up_scale", "e_down", "e_down_scale", "e_tensor_scale"):

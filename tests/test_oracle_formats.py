@@ -188,3 +188,82 @@ def test_prefetch_list_matches_bruteforce_sort():
     # hand case: counts 3,3,1 at experts 7,2,5 -> [2, 7, 5, then unused 0, 1, ...]
     ids = np.array([7, 2, 7, 2, 5, 7, 2], np.int32)
     assert orc.prefetch_list(ids, 10, 6).tolist() == [2, 7, 5, 0, 1, 3]
+
+
+# --- NVFP4 activation quantizer (SwiGLU output before the down projection) ----
+
+def _e4m3_positive_values():
+    return [orc.e4m3_value(c) for c in range(1, 0x7F)]
+
+
+def test_e4m3_rne_matches_torch_float8_on_values_midpoints_and_neighbours():
+    import torch
+    vals = _e4m3_positive_values()
+    xs = list(vals)
+    for a, b in zip(vals, vals[1:]):
+        m = (a + b) / 2.0                      # exact in fp32 (<= 5 significant bits)
+        xs += [m, np.nextafter(np.float32(m), np.float32(0)), np.nextafter(np.float32(m), np.float32(1e9))]
+    xs += [np.float32(2.0 ** -10), np.float32(2.0 ** -11), np.float32(3 * 2.0 ** -11)]
+    x = np.array(xs, np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([orc.e4m3_rne_sat(float(v)) for v in x], np.uint8)
+    assert np.array_equal(got, ref), x[got != ref][:8]
+    for big in (448.0, 460.0, 464.0, 1e4):
+        assert orc.e4m3_rne_sat(big) == 0x7E
+    assert orc.e4m3_rne_sat(0.0) == 0
+
+
+def _e2m1_bruteforce(y):
+    vals = [orc.e2m1_value(c) for c in range(8)]
+    a = abs(y)
+    if a > 6.0:
+        c = 7
+    else:
+        d = [abs(a - v) for v in vals]
+        best = min(d)
+        cand = [c for c in range(8) if d[c] == best]
+        c = cand[0] if len(cand) == 1 else [c for c in cand if c % 2 == 0][0]
+    return c | (8 if np.signbit(y) else 0)
+
+
+def test_e2m1_rne_matches_nearest_even_bruteforce():
+    vals = [orc.e2m1_value(c) for c in range(8)]
+    ys = []
+    for a, b in zip(vals, vals[1:]):
+        m = (a + b) / 2.0
+        ys += [m, float(np.nextafter(np.float32(m), np.float32(0))), float(np.nextafter(np.float32(m), np.float32(9)))]
+    ys += vals + [6.5, 7.0, 100.0, 1e-30, 0.0]
+    rng = np.random.default_rng(3)
+    ys += list(rng.uniform(0, 7, 400))
+    for y in ys + [-y for y in ys]:
+        y32 = float(np.float32(y))
+        assert orc.e2m1_rne_sat(y32) == _e2m1_bruteforce(y32), y32
+
+
+def test_nvfp4_quant16_closed_forms():
+    vals = np.array([orc.e2m1_value(c) for c in range(8)])
+    rng = np.random.default_rng(4)
+    for sc in (0x08, 0x30, 0x38, 0x41, 0x66):           # block scales 2^-6 .. 104
+        s = orc.e4m3_value(sc)
+        q = rng.integers(0, 16, 16)
+        x = np.where(q >= 8, -1.0, 1.0) * vals[q % 8] * s
+        x[int(rng.integers(0, 16))] = 6.0 * s           # amax = 6 s: the block scale is s itself
+        codes, scale, deq = orc.nvfp4_quant16(x.astype(np.float32))
+        assert scale == sc
+        assert np.array_equal(deq.astype(np.float64), x)
+    codes, scale, deq = orc.nvfp4_quant16(np.zeros(16, np.float32))
+    assert scale == 0 and not np.any(codes) and not np.any(deq)
+    # random blocks: every output is an E2M1 value times the block scale, the
+    # one the brute-force nearest-even rule picks for fl32(x / s)
+    for _ in range(50):
+        x = (rng.standard_normal(16) * 10.0 ** rng.uniform(-3, 2)).astype(np.float32)
+        codes, scale, deq = orc.nvfp4_quant16(x)
+        s = np.float32(orc.e4m3_value(scale))
+        assert s == np.float32(orc.e4m3_value(orc.e4m3_rne_sat(float(np.max(np.abs(x)) / np.float32(6.0)))))
+        if s == 0:  # the block scale underflows E4M3: the whole block is 0
+            assert not np.any(codes) and not np.any(deq)
+            continue
+        for i in range(16):
+            c = _e2m1_bruteforce(float(x[i] / s))
+            assert codes[i] == c
+            assert deq[i] == np.float32(orc.e2m1_value(c & 7) * (-1 if c & 8 else 1) * float(s))

@@ -187,3 +187,26 @@ def test_requests_are_independent():
     out2, st2 = orc.layer_forward(w2, lw, 2, W.T, [W.ctx, W.ctx], h2, k2, v2, W.cap, eps=W.eps)
     assert np.array_equal(out2[:W.T], out1) and np.array_equal(out2[W.T:], out1)
     assert np.array_equal(k2[0], k2[1])
+
+
+def test_act_fp4_expert_path_matches_library_composition():
+    """NVFP4 activations: recompute the experts from the pooled stage with
+    library matmuls and the pinned block quantizer."""
+    lw, k, v, h = _layer()
+    _, st = orc.layer_forward(W, lw, 1, W.T, [W.ctx], h, k.copy(), v.copy(), W.cap, eps=W.eps,
+                              act_fp4=True)
+    _, st0 = _run(lw, k.copy(), v.copy(), h)
+    acc = np.zeros((W.NT, W.P))
+    for t in range(W.NT):
+        for j in range(W.k):
+            e = int(st["ids"][t, j])
+            wgu, wd = _dense_expert(lw, e)
+            gu = st["p"][t] @ wgu.T
+            a = np.vectorize(orc.silu)(gu[:W.I]) * gu[W.I:]
+            aq = orc.nvfp4_quant_rows(a.astype(np.float32)[None, :])[0].astype(np.float64)
+            acc[t] += st["gates"][t, j] * (aq @ wd.T)
+    assert np.allclose(st["acc"], acc, rtol=1e-9, atol=1e-12)
+    # the quantization changes the result (fp4 keeps 8 magnitudes per block,
+    # so the change is of the order of the data itself, not of rounding)
+    d = np.abs(st["acc"] - st0["acc"]).max() / np.abs(st0["acc"]).max()
+    assert 1e-3 < d < 1.0, d
