@@ -43,6 +43,8 @@ def parse():
                     help="after timing, run one step with the self-timing kernel and print the phase breakdown")
     ap.add_argument("--tree", action="store_true",
                     help="verify a seeded random tree of candidate tokens per request instead of a chain")
+    ap.add_argument("--act-fp4", action="store_true",
+                    help="quantize the experts' SwiGLU outputs to NVFP4 before the down projection")
     ap.add_argument("--graph", action="store_true",
                     help="capture each step's msk_verify_step in a HIP graph and time the replays")
     ap.add_argument("--expert-prefetch", type=int, default=None,
@@ -119,7 +121,8 @@ def main():
     dev = "cuda"
     stream = torch.cuda.current_stream()
     t0 = time.time()
-    handle = msk.Handle(msk.make_config(w, expert_prefetch=args.expert_prefetch))
+    handle = msk.Handle(msk.make_config(w, expert_prefetch=args.expert_prefetch,
+                                        flags=msk.MSK_FLAG_ACT_FP4 if args.act_fp4 else 0))
     layers = []
     for l in range(w.n_layers):
         t = synth.device_layer(w, l, dev, stream_ptr=stream.cuda_stream)
@@ -231,6 +234,7 @@ def main():
             "pool": w.P, "expert_inter": w.I, "expert_format": "NVFP4 (E2M1 + E4M3/16 + fp32)",
             "dense_format": "bf16", "router": "fp32",
             "verify": "tree (seeded random parents)" if args.tree else "chain",
+            "expert_activations": "NVFP4 between the expert GEMMs" if args.act_fp4 else "fp16",
         },
         "achieved_tbps": round(mean_bytes / (mean_ms * 1e-3) / 1e12, 3),
         "hbm_frac": round(mean_bytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

@@ -70,6 +70,13 @@ typedef enum {
 
 /* msk_config.flags */
 #define MSK_FLAG_NO_NORM 0x1u /* skip both RMSNorms (special-case tests) */
+/* NVFP4 activations between the two expert GEMMs (orcarouter.ai, "Dove si
+ * colloca il confine del kernel": the output of the first expert GEMM travels
+ * as fp4). Each expert's SwiGLU output is quantized in blocks of 16 along the
+ * intermediate dim: block scale s = E4M3(amax / 6) (OCP E4M3FN, nearest even,
+ * saturating at 448), codes E2M1(x / s) (nearest even, saturating at 6, sign
+ * kept; 0 when s = 0), and the down projection reads E2M1(code) * s. */
+#define MSK_FLAG_ACT_FP4 0x2u
 
 typedef struct {
   int32_t hidden;        /* H, multiple of 128; nq*d also a multiple of 128 */
@@ -131,6 +138,12 @@ typedef struct {
   int32_t dq_expert; /* expert whose decoded weights are dumped (if selected) */
   uint16_t* dq_gate_up; /* f16 [2I][P]: E2M1 x E4M3 (tensor scale not applied) */
   uint16_t* dq_down;    /* f16 [P][I] */
+  /* With MSK_FLAG_ACT_FP4, for expert dq_expert (if selected), every token's
+   * SwiGLU output before quantization (gate weight not applied) and its
+   * NVFP4 encoding; tokens not routed to the expert are included. */
+  float* act;           /* fp32 [NT][I] */
+  uint8_t* act_codes;   /* [NT][I/2] E2M1, element 2m in the low nibble of byte m */
+  uint8_t* act_scales;  /* [NT][I/16] E4M3 block scales */
 } msk_debug;
 
 typedef struct {

@@ -173,6 +173,7 @@ std::string check_config(const msk_config* c) {
   if (c->max_requests <= 0 || c->max_requests > msk::kMaxReq) return "max_requests must be in 1..4";
   if (c->kv_capacity <= 0) return "kv_capacity must be positive";
   if (!(c->rms_eps >= 0.0f)) return "rms_eps must be >= 0";
+  if ((c->flags & ~(MSK_FLAG_NO_NORM | MSK_FLAG_ACT_FP4)) != 0) return "unknown flag bits";
   if (c->expert_prefetch < 0 || c->expert_prefetch > msk::kMaxPrefetch || c->expert_prefetch > c->n_experts)
     return "expert_prefetch must be in 0..min(32, n_experts)";
   return std::string();
@@ -244,8 +245,11 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
   {
     // GEMM1 stages 256 B per (selected expert, 8-row i-tile) unit of a workgroup in LDS
     const int64_t nsel = std::min<int64_t>(cfg->n_experts, (int64_t)pass_tokens(cfg) * cfg->top_k);
+    // (512 B per unit, in whole pairs of units, with activation quantization)
     const int64_t units = nsel * (cfg->expert_inter / 8);
-    if ((units + G - 1) / G * 256 > msk::kG1StageBytes)
+    const int64_t per_wg = (cfg->flags & MSK_FLAG_ACT_FP4) ? 2 * ((units / 2 + G - 1) / G) * 512
+                                                           : (units + G - 1) / G * 256;
+    if (per_wg > msk::kG1StageBytes)
       return fail(nullptr, MSK_E_SHAPE, "too many expert units per workgroup for the GEMM1 staging area");
   }
   Layout lay = make_layout(cfg, kMaxGrid);
@@ -424,6 +428,7 @@ msk::Params base_params(msk_handle h, const msk_io* io) {
   p.NT = io->n_requests * io->n_tokens;
   p.cap = c.kv_capacity;
   p.use_norm = (c.flags & MSK_FLAG_NO_NORM) ? 0 : 1;
+  p.act_fp4 = (c.flags & MSK_FLAG_ACT_FP4) ? 1 : 0;
   p.eps = c.rms_eps;
   for (int r = 0; r < io->n_requests; ++r) p.ctx[r] = io->ctx_len[r];
   p.q_slices = h->q_slices;
@@ -539,7 +544,7 @@ msk_status run_call(msk_handle h, int l0, int l1, const msk_io* io, hipStream_t 
       if (debug) {
         const msk_debug& d = *io->debug;
         p.dbg = msk::Debug{d.q, d.k_new, d.v_new, d.attn, d.h1, d.n2, d.logits, d.p, d.acc,
-                           d.dq_expert, d.dq_gate_up, d.dq_down};
+                           d.dq_expert, d.dq_gate_up, d.dq_down, d.act, d.act_codes, d.act_scales};
       }
       hipError_t e = msk_launch_layer(p, h->grid, debug, s);
       if (e != hipSuccess) return fail(h, MSK_E_HIP, std::string("layer launch failed: ") + hipGetErrorString(e));

@@ -80,6 +80,9 @@ struct Debug {
   int32_t dq_expert;
   uint16_t* dq_gu;
   uint16_t* dq_dn;
+  float* act;         // [NT][I] SwiGLU output of dq_expert before activation quantization
+  uint8_t* act_codes; // [NT][I/2] its E2M1 codes
+  uint8_t* act_sc;    // [NT][I/16] its E4M3 block scales
 };
 
 // Schedules of the dense phases, built once per handle and stored per
@@ -93,6 +96,7 @@ struct Params {
   int32_t H, nq, nkv, d, E, topk, P, I;
   int32_t R, T, NT, cap;
   int32_t use_norm;
+  int32_t act_fp4;        // SwiGLU outputs quantized to NVFP4 before the down projection
   float eps;
   int32_t ctx[kMaxReq];
   uint16_t tree[kMaxReq][kMaxTok];  // ancestor bitmask of each verify token (self included)

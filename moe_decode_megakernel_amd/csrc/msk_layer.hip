@@ -1526,6 +1526,66 @@ __device__ __forceinline__ uint32_t g1_step_scale(const uint4 (&sc)[2]) {
   return (x >> ((g_ & 1) * 16)) & 0xFFFFu;
 }
 
+// SwiGLU epilogue of one GEMM1 unit (local ordinal ul, selected slot j).
+// acc[q] = D[token 4g+q][column r]: gate (r < 8) or up (r >= 8) of i-row
+// it*8 + (r & 7). Without activation quantization the staged value is
+// fp16(a * gate weight), 256 B per unit; with it, the fp32 SwiGLU output a
+// itself, 512 B per unit, quantized block by block in the flush.
+__device__ __forceinline__ void g1_epilogue(const Params& p, const Route& rt, uint8_t* stage, int ul, int j,
+                                            f32x4_t acc) {
+  const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4;
+  const float ts = rt.ts_gu[j];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float up = __shfl_xor(acc[q], 8);
+    const int tok = 4 * g_ + q;
+    if (r_ < 8) {
+      const float gate = acc[q] * ts;
+      const float a = gate / (1.0f + expf(-gate)) * (up * ts);
+      if (p.act_fp4) {
+        reinterpret_cast<float*>(stage + (size_t)ul * 512)[tok * 8 + r_] = a;
+      } else {
+        reinterpret_cast<uint16_t*>(stage + (size_t)ul * 256)[tok * 8 + r_] = f2h(a * rt.tokgate[j][tok]);
+      }
+    }
+  }
+}
+
+// NVFP4 quantization of the SwiGLU output (orcarouter.ai, "Dove si colloca il
+// confine del kernel": the activations leave the first expert GEMM as fp4).
+// One block = 16 consecutive fp32 values along the expert's intermediate
+// dim. Block scale s = E4M3(amax / 6), nearest even, saturating at 448;
+// code = E2M1(x / s), nearest even, saturating at 6, sign kept (0 when
+// s = 0); value = E2M1(code) * s, exact in fp32.
+//
+// fp32 -> OCP E4M3FN code for x >= 0.
+__device__ __forceinline__ uint32_t e4m3_code_rne_sat(float x) {
+  if (!(x > 0.0f)) return 0u;
+  if (x >= 448.0f) return 0x7Eu;
+  if (x < 0.015625f) return (uint32_t)__builtin_rintf(x * 512.0f);  // 2^-9 grid; 8 is the smallest normal
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  u += 0x7FFFFu + ((u >> 20) & 1u);  // significand to 3 bits, ties to even (a carry bumps the exponent)
+  return min((((u >> 23) - 120u) << 3) | ((u >> 20) & 7u), 0x7Eu);  // exponent bias 127 -> 7
+}
+
+// fp32 -> E2M1 code (bit 3 = sign). On [0,2) the grid is 0.5, on [2,4) it
+// is 1, from 4 on it is 2 (only 4 and 6 exist).
+__device__ __forceinline__ uint32_t e2m1_code_rne_sat(float y) {
+  const uint32_t sgn = (__builtin_bit_cast(uint32_t, y) >> 28) & 8u;
+  const float a = fminf(fabsf(y), 8.0f);
+  uint32_t c;
+  if (a < 2.0f) c = (uint32_t)__builtin_rintf(a * 2.0f);
+  else if (a < 4.0f) c = 2u + (uint32_t)__builtin_rintf(a);
+  else c = min(4u + (uint32_t)__builtin_rintf(a * 0.5f), 7u);
+  return sgn | c;
+}
+
+// E2M1 code -> value (twice the magnitude of codes 0..7 is 0,1,2,3,4,6,8,12).
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const float m = (float)((0xC8643210u >> ((c & 7u) * 4u)) & 15u) * 0.5f;
+  return (c & 8u) ? -m : m;
+}
+
 template <bool debug>
 __device__ __forceinline__ void gemm1_units16(const Params& p, Smem& sm, const Route& rt, int u0, int my_units,
                                               int w) {
@@ -1571,19 +1631,7 @@ __device__ __forceinline__ void gemm1_units16(const Params& p, Smem& sm, const R
     G1_STEP(0) G1_STEP(1) G1_STEP(2) G1_STEP(3) G1_STEP(4) G1_STEP(5) G1_STEP(6) G1_STEP(7)
     G1_STEP(8) G1_STEP(9) G1_STEP(10) G1_STEP(11) G1_STEP(12) G1_STEP(13) G1_STEP(14) G1_STEP(15)
 #undef G1_STEP
-    // acc[q] = D[token 4g+q][column r]: gate (r < 8) or up (r >= 8) of i-row it*8 + (r & 7).
-    const float ts = rt.ts_gu[j];
-    uint16_t* srow = reinterpret_cast<uint16_t*>(stage + (size_t)(u - u0) * 256);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float up = __shfl_xor(acc[q], 8);
-      const int tok = 4 * g_ + q;
-      if (r_ < 8) {
-        const float gate = acc[q] * ts;
-        const float a = gate / (1.0f + expf(-gate)) * (up * ts);
-        srow[tok * 8 + r_] = f2h(a * rt.tokgate[j][tok]);
-      }
-    }
+    g1_epilogue(p, rt, stage, u - u0, j, acc);
   }
 }
 
@@ -1595,8 +1643,12 @@ __device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
   const int I = p.I, P = p.P, ntile = I / 8, nsteps = P / 128;
   const int U = rt.n_sel * ntile;
-  const int u0 = (int)((long long)blockIdx.x * U / gridDim.x);
-  const int u1 = (int)((long long)(blockIdx.x + 1) * U / gridDim.x);
+  // with activation quantization a workgroup owns whole pairs of units (one
+  // 16-wide block of the intermediate dim; ntile is even, so a pair never
+  // spans two experts)
+  const int pu = p.act_fp4 ? 2 : 1;
+  const int u0 = pu * (int)((long long)blockIdx.x * (U / pu) / gridDim.x);
+  const int u1 = pu * (int)((long long)(blockIdx.x + 1) * (U / pu) / gridDim.x);
   const int my_units = (u1 - u0 - w + kWaves - 1) / kWaves;  // units u0 + w + 8*m < u1
   const int total = my_units > 0 ? my_units * nsteps : 0;
   if (total > 0 && nsteps == kG1UnitSteps) {
@@ -1645,20 +1697,8 @@ __device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
             }
           }
           if (cst == nsteps - 1) {
-            // acc[q] = D[token 4g+q][column r]: gate (r < 8) or up (r >= 8) of i-row it*8 + (r & 7).
             const int u = u0 + w + kWaves * cm, j = u / ntile;
-            const float ts = rt.ts_gu[j];
-            uint16_t* srow = reinterpret_cast<uint16_t*>(stage + (size_t)(u - u0) * 256);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float up = __shfl_xor(acc[q], 8);
-              const int tok = 4 * g_ + q;
-              if (r_ < 8) {
-                const float gate = acc[q] * ts;
-                const float a = gate / (1.0f + expf(-gate)) * (up * ts);
-                srow[tok * 8 + r_] = f2h(a * rt.tokgate[j][tok]);
-              }
-            }
+            g1_epilogue(p, rt, stage, u - u0, j, acc);
             acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
             cst = 0;
             ++cm;
@@ -1672,13 +1712,55 @@ __device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
     }
   }
   __syncthreads();
-  // flush: 16 B per (unit, token) to abuf[j][token][it*8 .. +8]
   const int NT = p.NT;
-  for (int q = threadIdx.x; q < (u1 - u0) * NT; q += kThreads) {
-    const int ul = q / NT, tok = q - ul * NT;
-    const int u = u0 + ul, j = u / ntile, it = u - j * ntile;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (size_t)ul * 256 + tok * 16);
-    st_wt16(p.abuf + ((size_t)j * NT + tok) * I + it * 8, v);
+  if (p.act_fp4) {
+    // quantize: one (unit pair, token) block of 16 per item, 32 B to
+    // abuf[j][token][it*8 .. +16] as fp16(value * gate weight)
+    for (int q = threadIdx.x; q < (u1 - u0) / 2 * NT; q += kThreads) {
+      const int pl = q / NT, tok = q - pl * NT;
+      const int u = u0 + 2 * pl, j = u / ntile, it = u - j * ntile;
+      const float* s0 = reinterpret_cast<const float*>(stage + (size_t)(2 * pl) * 512) + tok * 8;
+      const float* s1 = reinterpret_cast<const float*>(stage + (size_t)(2 * pl + 1) * 512) + tok * 8;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[i] = s0[i];
+        x[8 + i] = s1[i];
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+      const uint32_t sc = e4m3_code_rne_sat(amax / 6.0f);
+      const float s = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
+      const float gw = rt.tokgate[j][tok];
+      uint32_t codes[2] = {0u, 0u}, hv[8];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t c = e2m1_code_rne_sat(s > 0.0f ? x[i] / s : 0.0f);
+        codes[i >> 3] |= c << ((i & 7) * 4);
+        const uint16_t h = f2h(e2m1_value(c) * s * gw);
+        hv[i >> 1] = (i & 1) ? (hv[i >> 1] | ((uint32_t)h << 16)) : (uint32_t)h;
+      }
+      uint16_t* dst = p.abuf + ((size_t)j * NT + tok) * I + it * 8;
+      st_wt16(dst, u32x4_t{hv[0], hv[1], hv[2], hv[3]});
+      st_wt16(dst + 8, u32x4_t{hv[4], hv[5], hv[6], hv[7]});
+      if constexpr (debug) {
+        if (p.dbg.act && rt.sel[j] == p.dbg.dq_expert) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) p.dbg.act[(size_t)tok * I + it * 8 + i] = x[i];
+          *reinterpret_cast<uint2*>(p.dbg.act_codes + (size_t)tok * (I / 2) + it * 4) = make_uint2(codes[0], codes[1]);
+          p.dbg.act_sc[(size_t)tok * (I / 16) + it / 2] = (uint8_t)sc;
+        }
+      }
+    }
+  } else {
+    // 16 B per (unit, token) to abuf[j][token][it*8 .. +8]
+    for (int q = threadIdx.x; q < (u1 - u0) * NT; q += kThreads) {
+      const int ul = q / NT, tok = q - ul * NT;
+      const int u = u0 + ul, j = u / ntile, it = u - j * ntile;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (size_t)ul * 256 + tok * 16);
+      st_wt16(p.abuf + ((size_t)j * NT + tok) * I + it * 8, v);
+    }
   }
   __syncthreads();
 }

@@ -15,6 +15,7 @@ MSK_OK, MSK_E_INVALID, MSK_E_SHAPE, MSK_E_ALIGN, MSK_E_STATE, MSK_E_CAPACITY, MS
 STATUS_NAMES = ["MSK_OK", "MSK_E_INVALID", "MSK_E_SHAPE", "MSK_E_ALIGN", "MSK_E_STATE",
                 "MSK_E_CAPACITY", "MSK_E_HIP", "MSK_E_TIMEOUT"]
 MSK_FLAG_NO_NORM = 0x1
+MSK_FLAG_ACT_FP4 = 0x2
 
 EXPORTS = ("msk_workspace_bytes", "msk_create", "msk_load_layer", "msk_verify_layer",
            "msk_verify_step", "msk_destroy", "msk_down_scale_bytes", "msk_pack_down_scale",
@@ -41,7 +42,8 @@ DEBUG_PTRS = ("q", "k_new", "v_new", "attn", "h1", "n2", "logits", "p", "acc")
 
 
 class msk_debug(ctypes.Structure):
-    _fields_ = [(n, vp) for n in DEBUG_PTRS] + [("dq_expert", i32), ("dq_gate_up", vp), ("dq_down", vp)]
+    _fields_ = [(n, vp) for n in DEBUG_PTRS] + [("dq_expert", i32), ("dq_gate_up", vp), ("dq_down", vp),
+                                                ("act", vp), ("act_codes", vp), ("act_scales", vp)]
 
 
 class msk_io(ctypes.Structure):
@@ -185,7 +187,8 @@ def make_io(n_requests, n_tokens, ctx: Sequence[int], h_in, h_out, expert_ids=No
 
 
 def make_debug(t: Dict, dq_expert: int = -1) -> msk_debug:
-    d = msk_debug(dq_expert=dq_expert, dq_gate_up=_ptr(t.get("dq_gate_up")), dq_down=_ptr(t.get("dq_down")))
+    d = msk_debug(dq_expert=dq_expert, dq_gate_up=_ptr(t.get("dq_gate_up")), dq_down=_ptr(t.get("dq_down")),
+                  act=_ptr(t.get("act")), act_codes=_ptr(t.get("act_codes")), act_scales=_ptr(t.get("act_scales")))
     for n in DEBUG_PTRS:
         setattr(d, n, _ptr(t.get(n)))
     return d

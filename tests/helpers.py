@@ -56,6 +56,9 @@ class GpuLayerRun:
             "acc": torch.zeros((NT, w.P), **f32),
             "dq_gate_up": torch.zeros((2 * w.I, w.P), dtype=torch.int16, device=dev),
             "dq_down": torch.zeros((w.P, w.I), dtype=torch.int16, device=dev),
+            "act": torch.zeros((NT, w.I), **f32),
+            "act_codes": torch.zeros((NT, w.I // 2), dtype=torch.uint8, device=dev),
+            "act_scales": torch.zeros((NT, w.I // 16), dtype=torch.uint8, device=dev),
         }
         self.ctx = [w.ctx] * w.R if ctx is None else list(ctx)
         self.dq_expert = dq_expert
@@ -79,11 +82,11 @@ class GpuLayerRun:
         self.handle.close()
 
 
-def oracle_layer(w, lw, k, v, h, use_norm=True, ctx=None, tree=None):
+def oracle_layer(w, lw, k, v, h, use_norm=True, ctx=None, tree=None, act_fp4=False):
     ctx = [w.ctx] * w.R if ctx is None else list(ctx)
     kk, vv = k.copy(), v.copy()
     out, st = orc.layer_forward(w, lw, w.R, w.T, ctx, np.asarray(h, np.float64), kk, vv, w.cap,
-                                eps=w.eps, use_norm=use_norm, tree=tree)
+                                eps=w.eps, use_norm=use_norm, tree=tree, act_fp4=act_fp4)
     st["h_out"] = out
     st["k_cache"] = kk
     st["v_cache"] = vv

@@ -112,5 +112,15 @@ def test_no_scalar_cache_writes(kernel_asm):
 
 
 def test_no_scratch_spills(kernel_asm):
-    spills = [int(m) for m in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", kernel_asm)]
-    assert spills and max(spills) == 0, f"private segment sizes: {spills}"
+    """No kernel spills registers to scratch, and the production and
+    self-timing variants of the layer kernel use no private memory at all.
+    The stage-dump variant (template argument 1) may keep a private copy of
+    its argument block (<= 1 KiB): it runs in parity tests only."""
+    names = re.findall(r"^\s+\.name:\s+(\S+)", kernel_asm, re.M)
+    priv = [int(m) for m in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", kernel_asm)]
+    vspill = [int(m) for m in re.findall(r"\.vgpr_spill_count:\s+(\d+)", kernel_asm)]
+    assert names and len(names) == len(priv) == len(vspill), (len(names), len(priv), len(vspill))
+    for n, pv, vs in zip(names, priv, vspill):
+        assert vs == 0, (n, "vgpr spills", vs)
+        limit = 1024 if re.search(r"layer_kernelILj\d+ELi1EE", n) else 0
+        assert pv <= limit, (n, "private segment", pv)

@@ -1,0 +1,186 @@
+"""GPU parity of the NVFP4 activations between the two expert GEMMs
+(MSK_FLAG_ACT_FP4; orcarouter.ai, "Dove si colloca il confine del kernel":
+the first expert GEMM's output travels as fp4) against the oracle.
+
+Bit-exact: the kernel's block scales and E2M1 codes equal the oracle's
+quantizer applied to the kernel's own fp32 SwiGLU outputs (the quantizer is
+an exact function of its input).
+
+Decisions against the oracle's own activations: the pre-quantization SwiGLU
+outputs agree within the float tolerance, and a code (or a block scale) may
+differ from the oracle's only where the rounding threshold between the two
+codes lies between the oracle's and the kernel's input value. Such a flip
+moves one value by a whole grid step, so the quantized expert sum is not
+within the max-error bound of a continuous function; it is checked by its
+RMS error, and the layer output by the max-error bound."""
+import numpy as np
+import pytest
+
+from moe_decode_megakernel_amd import msk, synth
+from oracle import oracle as orc
+from tests.helpers import GpuLayerRun, oracle_layer, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2  # max |err| <= TOL * RMS(reference), fp32 accumulation on both sides
+
+
+def _inputs(w):
+    lw = synth.layer_weights(w, 0)
+    k, v = synth.kv_cache(w, 0)
+    h = synth.h_input(w, 0)
+    return lw, k, v, h
+
+
+def _check_quant_dump(w, g, e, label):
+    act, codes, sc = g["act"], g["act_codes"], g["act_scales"]
+    assert np.any(act != 0.0), (label, "expert not dumped", e)
+    for t in range(w.NT):
+        for b in range(0, w.I, 16):
+            oc, osc, _ = orc.nvfp4_quant16(act[t, b:b + 16])
+            packed = (oc[0::2] | (oc[1::2] << 4)).astype(np.uint8)
+            assert np.array_equal(codes[t, b // 2:b // 2 + 8], packed), (label, e, t, b)
+            assert int(sc[t, b // 16]) == osc, (label, e, t, b)
+    n_scales = len(np.unique(sc))
+    say(f"[{label}] expert {e}: {w.NT * w.I // 16} blocks bit-exact, {n_scales} distinct scales")
+
+
+ACC_RMS_TOL = 5e-2  # RMS(acc err) / RMS(acc) with NVFP4 activations (code flips)
+
+
+def _rms_rel(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.sqrt(np.mean((got - ref) ** 2)) / np.sqrt(np.mean(ref * ref)))
+
+
+def _check_layer(w, g, o, o_plain, label):
+    errs = {k: rel_err(g[k], o[k]) for k in ("p", "h_out")}
+    acc_max = rel_err(g["acc"], o["acc"])
+    acc_rms = _rms_rel(g["acc"], o["acc"])
+    # the quantization's own effect, for scale: oracle with vs without it
+    effect = _rms_rel(o["acc"], o_plain["acc"])
+    say(f"[{label}] rel errs " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) +
+        f" acc max={acc_max:.2e} rms={acc_rms:.2e}; oracle fp4-vs-unquantized acc rms {effect:.2e}")
+    for k, e in errs.items():
+        assert e <= TOL, (label, k, e)
+    assert acc_rms <= ACC_RMS_TOL, (label, "acc rms", acc_rms)
+    # the kernel follows the quantized oracle far more closely than the
+    # quantization moves the result
+    assert acc_rms < 0.25 * effect, (label, acc_rms, effect)
+
+
+def _silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def _oracle_act(w, lw, o, e):
+    """The oracle's SwiGLU output of expert e for every token, before
+    quantization: its pooled vector times the dequantized gate/up weights
+    (library matmul over the oracle's stages), rounded to fp32 as the
+    oracle's quantizer takes it."""
+    wgu = orc.nvfp4_dequant(lw["e_gate_up"][e], lw["e_gate_up_scale"][e], float(lw["e_tensor_scale"][e, 0]),
+                            2 * w.I, w.P)
+    gu = np.asarray(o["p"], np.float64) @ wgu.T
+    return (_silu(gu[:, :w.I]) * gu[:, w.I:]).astype(np.float32)
+
+
+def _between(a, b, t):
+    lo, hi = min(a, b), max(a, b)
+    return lo <= t <= hi
+
+
+def _check_decisions(w, g, xo_all, e, label):
+    """Kernel codes vs the oracle's codes of its own activations: equal, or
+    a neighbouring code whose rounding threshold lies between the two
+    inputs. Returns (blocks, flipped scales, flipped codes)."""
+    xg_all = g["act"]
+    n_blk = n_sc = n_code = 0
+    for t in range(w.NT):
+        for b in range(0, w.I, 16):
+            xo, xg = xo_all[t, b:b + 16], xg_all[t, b:b + 16]
+            co, so, _ = orc.nvfp4_quant16(xo)
+            cg, sg, _ = orc.nvfp4_quant16(xg)
+            n_blk += 1
+            if so != sg:
+                # scales: neighbouring E4M3 codes, their midpoint between the two amax/6
+                assert abs(so - sg) == 1, (label, e, t, b, so, sg)
+                mid = 0.5 * (orc.e4m3_value(so) + orc.e4m3_value(sg))
+                ao = float(np.float32(np.max(np.abs(xo))) / np.float32(6.0))
+                ag = float(np.float32(np.max(np.abs(xg))) / np.float32(6.0))
+                assert _between(ao, ag, mid), (label, e, t, b, ao, ag, mid)
+                n_sc += 1
+                continue
+            s = orc.e4m3_value(so)
+            for i in np.nonzero(co != cg)[0]:
+                vo, vg = orc.e2m1_value(int(co[i])), orc.e2m1_value(int(cg[i]))
+                if vo == vg:
+                    continue  # +0 and -0: a value that rounds to zero from either side
+                # same side of zero (or zero), adjacent magnitudes on the E2M1 grid
+                grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+                mo, mg = abs(vo), abs(vg)
+                assert abs(grid.index(mo) - grid.index(mg)) == 1, (label, e, t, b, i, vo, vg)
+                thr = 0.5 * (mo + mg)
+                yo = abs(float(np.float32(xo[i]) / np.float32(s)))
+                yg = abs(float(np.float32(xg[i]) / np.float32(s)))
+                assert _between(yo, yg, thr), (label, e, t, b, i, yo, yg, thr)
+                n_code += 1
+    say(f"[{label}] expert {e}: {n_blk} blocks, {n_sc} scale flips, {n_code} code flips at thresholds")
+    return n_blk, n_sc, n_code
+
+
+def test_tiny_act_fp4_quantizer_and_layer():
+    w = synth.WORKLOADS["tiny_swa"]
+    lw, k, v, h = _inputs(w)
+    o = oracle_layer(w, lw, k, v, h, act_fp4=True)
+    o_plain = oracle_layer(w, lw, k, v, h)
+    experts = list(dict.fromkeys(int(e) for e in o["ids"].reshape(-1)))[:4]
+    run = GpuLayerRun(w, lw, k, v, h, flags=msk.MSK_FLAG_ACT_FP4)
+    for i, e in enumerate(experts):
+        say(f"[tiny-fp4] gpu run, dumped expert {e}")
+        run.dq_expert = e
+        g = run.run()
+        _check_quant_dump(w, g, e, "tiny-fp4")
+        xo = _oracle_act(w, lw, o, e)
+        assert rel_err(g["act"], xo) <= TOL
+        _check_decisions(w, g, xo, e, "tiny-fp4")
+        if i == 0:
+            assert np.array_equal(g["ids"], o["ids"]), "routing differs from the oracle on this seed"
+            _check_layer(w, g, o, o_plain, "tiny-fp4")
+    run.close()
+
+
+def test_act_fp4_off_is_unchanged_and_on_is_deterministic():
+    w = synth.WORKLOADS["tiny_swa"]
+    lw, k, v, h = _inputs(w)
+    a = GpuLayerRun(w, lw, k, v, h)
+    plain = a.run(debug=False)
+    a.close()
+    b = GpuLayerRun(w, lw, k, v, h, flags=msk.MSK_FLAG_ACT_FP4)
+    q1 = b.run(debug=False)
+    q2 = b.run(debug=False)
+    b.close()
+    assert np.array_equal(q1["h_out"], q2["h_out"])
+    assert not np.array_equal(q1["h_out"], plain["h_out"]), "the flag changed nothing"
+
+
+def test_working_size_act_fp4_layer():
+    w = synth.WORKLOADS["swa_layer"]
+    say("[swa-fp4] generating inputs")
+    lw, k, v, h = _inputs(w)
+    say("[swa-fp4] oracle runs")
+    o = oracle_layer(w, lw, k, v, h, act_fp4=True)
+    o_plain = oracle_layer(w, lw, k, v, h)
+    e = int(o["ids"][0, 0])
+    say(f"[swa-fp4] gpu run, dumped expert {e}")
+    run = GpuLayerRun(w, lw, k, v, h, flags=msk.MSK_FLAG_ACT_FP4, dq_expert=e)
+    g = run.run()
+    run.close()
+    _check_quant_dump(w, g, e, "swa-fp4")
+    xo = _oracle_act(w, lw, o, e)
+    say(f"[swa-fp4] act rel err {rel_err(g['act'], xo):.2e}")
+    assert rel_err(g["act"], xo) <= TOL
+    _, n_sc, n_code = _check_decisions(w, g, xo, e, "swa-fp4")
+    assert n_sc + n_code <= 0.01 * w.NT * w.I, "more flips than the activation error explains"
+    assert np.array_equal(np.sort(g["ids"], axis=1), np.sort(o["ids"], axis=1)), "selection differs"
+    _check_layer(w, g, o, o_plain, "swa-fp4")
