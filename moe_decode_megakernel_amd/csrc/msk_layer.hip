@@ -1208,12 +1208,34 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __builtin_popcountll(m); }
 
+// Inverse of order_key on its image (-0 comes back as +0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Wave-wide maximum (uniform result): DPP within 16-lane rows, then the four
+// rows' maxima by read-lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));  // row_mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
 // Top-k by (logit descending, index ascending); gates = softmax of the
-// selected logits. One wave per token: the k-th largest key is found by a
-// radix select over the 32 key bits (a ballot and popcount per bit), the
-// selected set is every key above it plus the lowest-index ties, and the
-// selected entries are ranked in LDS. The routing tables are then built
-// without serial loops.
+// selected logits. One wave per two tokens: the k entries are extracted one
+// by one (wave-wide maximum of order-preserving keys, lowest index among
+// equal keys), which ranks them as they come. The routing tables are then
+// built without serial loops.
 // The routing inputs of this thread: the logits of the wave's two tokens and
 // the tensor scales of expert threadIdx.x, requested before the pooled
 // activation fill so the round trips overlap.
@@ -1255,6 +1277,56 @@ __device__ __forceinline__ float route_logit(const RouteLoads& L, int S, int tt,
   return r + L.bias[j];
 }
 
+// The pooled-activation fill of the routing phase in two steps, so that its
+// loads are in flight while the top-k runs: X = fp16 of the sum over the
+// n <= kMaxPSlices slices of fp32 [n][NT][K], in slice order from +0 (the
+// arithmetic of fill_x_sum), items as in fill_x_sum, kSumBatch items per
+// thread per batch (one batch covers K <= 2048). Loads are unconditional
+// (slice and token indices clamped in range).
+constexpr int kSumBatch = 8;
+static_assert(kSumBatch * kThreads >= kMaxTok * 2048 / 8, "one batch covers the pooled tile");
+struct SumLoads {
+  float4 a[kMaxPSlices][kSumBatch], b[kMaxPSlices][kSumBatch];
+};
+
+__device__ __forceinline__ void fill_sum_issue(const float* parts, int n, int K, int NT, int i0, SumLoads& L) {
+  const int K8 = K / 8;
+#pragma unroll
+  for (int u = 0; u < kMaxPSlices; ++u)
+#pragma unroll
+    for (int q = 0; q < kSumBatch; ++q) {
+      const int i = i0 + q * kThreads;
+      const int t = min(i / K8, NT - 1), k = (i % K8) * 8;
+      const float4* src = reinterpret_cast<const float4*>(parts + ((size_t)min(u, n - 1) * NT + t) * K + k);
+      L.a[u][q] = src[0];
+      L.b[u][q] = src[1];
+    }
+}
+
+__device__ __forceinline__ void fill_sum_finish(const SumLoads& L, int n, int K, int NT, int i0, Smem& sm) {
+  const int K8 = K / 8, total = kMaxTok * K8;
+#pragma unroll
+  for (int q = 0; q < kSumBatch; ++q) {
+    const int i = i0 + q * kThreads;
+    if (i >= total) break;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kMaxPSlices; ++u) {
+      if (u < n) {
+        v[0] += L.a[u][q].x; v[1] += L.a[u][q].y; v[2] += L.a[u][q].z; v[3] += L.a[u][q].w;
+        v[4] += L.b[u][q].x; v[5] += L.b[u][q].y; v[6] += L.b[u][q].z; v[7] += L.b[u][q].w;
+      }
+    }
+    const int t = i / K8, k = (i % K8) * 8;
+    uint4 out = make_uint4(0, 0, 0, 0);
+    if (t < NT) {
+      out.x = pack2(f2h(v[0]), f2h(v[1])); out.y = pack2(f2h(v[2]), f2h(v[3]));
+      out.z = pack2(f2h(v[4]), f2h(v[5])); out.w = pack2(f2h(v[6]), f2h(v[7]));
+    }
+    *reinterpret_cast<uint4*>(sm.x + t * x_stride(K) + k * 2) = out;
+  }
+}
+
 template <bool debug>
 __device__ __forceinline__ void routing(const Params& p, Smem& sm, bool write_out, const RouteLoads& in) {
   Route& rt = route_of(sm);
@@ -1281,40 +1353,50 @@ __device__ __forceinline__ void routing(const Params& p, Smem& sm, bool write_ou
     }
   }
   __syncthreads();
-  // Threshold of each of the wave's tokens, bit by bit from the top, both
-  // tokens in one loop: T grows to the largest prefix value with at least K
-  // keys >= T. Once exactly K keys are >= T the selected set is fixed and that
-  // token stops (ties below T cannot enter).
+  // Top-k by repeated extraction, both tokens of the wave interleaved: the
+  // wave-wide largest key, and among equal keys the lowest expert index
+  // (index = lane + 64 j, so the first j with a hit, then its lowest lane),
+  // is taken and removed, K times. The extraction order is the ranking
+  // (value descending, index ascending); rank r's expert and logit end up in
+  // lane r.
   uint32_t key[TPW][kMaxE / 64];
-  uint32_t Tt[TPW];
-  bool done[TPW];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const bool live = w + tt * kWaves < NT;
 #pragma unroll
     for (int j = 0; j < kMaxE / 64; ++j) key[tt][j] = (live && lane + j * 64 < E) ? order_key(v[tt][j]) : 0u;
-    Tt[tt] = 0;
-    done[tt] = !live;
   }
-#pragma unroll 4
-  for (int b = 31; b >= 0; --b) {
-    bool all = true;
+  int rid[TPW];
+  float rval[TPW];
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) all = all && done[tt];
-    if (all) break;
-    int cnt[TPW];
+  for (int tt = 0; tt < TPW; ++tt) {
+    rid[tt] = 0;
+    rval[tt] = 0.0f;
+  }
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-      const uint32_t cand = Tt[tt] | (1u << b);
-      cnt[tt] = 0;
-#pragma unroll
-      for (int j = 0; j < kMaxE / 64; ++j) cnt[tt] += popc64(__ballot(key[tt][j] >= cand));
-    }
+  for (int r = 0; r < kMaxK; ++r) {
+    if (r >= K) break;
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-      if (!done[tt] && cnt[tt] >= K) {
-        Tt[tt] |= 1u << b;
-        done[tt] = cnt[tt] == K;
+      uint32_t lm = key[tt][0];
+#pragma unroll
+      for (int j = 1; j < kMaxE / 64; ++j) lm = max(lm, key[tt][j]);
+      const uint32_t m = wave_max_u32(lm);
+      int jsel = kMaxE / 64, lsel = 0;
+#pragma unroll
+      for (int j = kMaxE / 64 - 1; j >= 0; --j) {
+        const uint64_t hit = __ballot(key[tt][j] == m);
+        if (hit) {
+          jsel = j;
+          lsel = __builtin_ctzll(hit);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxE / 64; ++j)
+        if (j == jsel && lane == lsel) key[tt][j] = 0u;
+      if (lane == r) {
+        rid[tt] = lsel + 64 * jsel;
+        rval[tt] = key_value(m);
       }
     }
   }
@@ -1322,67 +1404,16 @@ __device__ __forceinline__ void routing(const Params& p, Smem& sm, bool write_ou
   for (int tt = 0; tt < TPW; ++tt) {
     const int t = w + tt * kWaves;
     if (t >= NT) break;
-    const uint32_t T = Tt[tt];
-    const uint32_t (&kk)[kMaxE / 64] = key[tt];
-    int n_gt = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxE / 64; ++j) n_gt += popc64(__ballot(kk[j] > T));
-    int ties_before = 0;  // ties with a lower index (index = lane + 64*j)
-    bool sel[kMaxE / 64];
-#pragma unroll
-    for (int j = 0; j < kMaxE / 64; ++j) {
-      const uint64_t tie = __ballot(kk[j] == T);
-      const int my_rank = ties_before + popc64(tie & lt_mask);
-      sel[j] = kk[j] > T || (kk[j] == T && my_rank < K - n_gt);
-      ties_before += popc64(tie);
-    }
-    // The K selected, in index order, moved to lanes 0..K-1 by forward lane
-    // permutes (unselected lanes write to lane 63, never read).
-    float mv = 0.0f;
-    int me = 0;
-    {
-      int base = 0;
-#pragma unroll
-      for (int j = 0; j < kMaxE / 64; ++j) {
-        const uint64_t m = __ballot(sel[j]);
-        const int n = popc64(m);
-        const int dst = (sel[j] ? base + popc64(m & lt_mask) : 63) * 4;
-        const int pv = __builtin_amdgcn_ds_permute(dst, __builtin_bit_cast(int, v[tt][j]));
-        const int pe = __builtin_amdgcn_ds_permute(dst, lane + j * 64);
-        if (lane >= base && lane < base + n) {
-          mv = __builtin_bit_cast(float, pv);
-          me = pe;
-        }
-        base += n;
-      }
-    }
-    // rank among the selected (value descending, index ascending) and the
-    // largest selected value, from read-lanes of lanes 0..K-1
-    const uint32_t mk = order_key(mv);
-    int rank = 0;
-    float mx = mv;
-#pragma unroll
-    for (int q = 0; q < kMaxK; ++q) {
-      if (q < K) {
-        const float ov = readlane_f32(mv, q);
-        const int oe = __builtin_amdgcn_readlane(me, q);
-        const uint32_t ok = order_key(ov);
-        rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
-        mx = fmaxf(mx, ov);
-      }
-    }
-    // ids and softmax numerators to lane = rank; the sum in rank order
-    const float ev = expf(mv - mx);
-    const int rdst = (lane < K ? rank : 63) * 4;
-    const int rid = __builtin_amdgcn_ds_permute(rdst, me);
-    const float re = __builtin_bit_cast(float, __builtin_amdgcn_ds_permute(rdst, __builtin_bit_cast(int, ev)));
+    // gates: softmax of the selected logits, max-subtracted, summed in rank order
+    const float mx = readlane_f32(rval[tt], 0);
+    const float ev = expf(rval[tt] - mx);
     float ssum = 0.0f;
 #pragma unroll
     for (int q = 0; q < kMaxK; ++q)
-      if (q < K) ssum += readlane_f32(re, q);
+      if (q < K) ssum += readlane_f32(ev, q);
     if (lane < K) {
-      rt.ids[t][lane] = rid;
-      rt.gates[t][lane] = re / ssum;
+      rt.ids[t][lane] = rid[tt];
+      rt.gates[t][lane] = ev / ssum;
     }
   }
   __syncthreads();
@@ -2065,9 +2096,20 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
 
   // routing (every workgroup) + experts' gate/up
   {
+    // logits first, then the first batch of the pooled activations, whose
+    // loads stay in flight while the top-k runs (routing touches only the
+    // route tables, which lie after the pooled tile in LDS)
     const RouteLoads rl = routing_issue(p);
-    fill_x_sum(p.ppart, p.p_slices, p.P, p.NT, sm);
+    SumLoads sl;
+    fill_sum_issue(p.ppart, p.p_slices, p.P, p.NT, threadIdx.x, sl);
     routing<DEBUG>(p, sm, blockIdx.x == 0, rl);
+    fill_sum_finish(sl, p.p_slices, p.P, p.NT, threadIdx.x, sm);
+    for (int i0 = threadIdx.x + kSumBatch * kThreads; i0 < kMaxTok * (p.P / 8); i0 += kSumBatch * kThreads) {
+      fill_sum_issue(p.ppart, p.p_slices, p.P, p.NT, i0, sl);
+      fill_sum_finish(sl, p.p_slices, p.P, p.NT, i0, sm);
+    }
+    vm_drain();
+    __syncthreads();
   }
   mark(kTrRouting);
   if (DEBUG && blockIdx.x == 0) {
