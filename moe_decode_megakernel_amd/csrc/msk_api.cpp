@@ -18,7 +18,7 @@ namespace {
 using msk::kMaxGrid;
 
 struct Layout {
-  size_t bar, err, zeros, sched, h1, ssq1, ssq2, hbuf0, hbuf1, qpart, apart, attn, logits, ppart, abuf, accpart, hist;
+  size_t bar, err, zeros, sched, h1, ssq1, ssq2, hbuf0, hbuf1, qpart, apart, attn, xq, logits, ppart, abuf, accpart, hist;
   size_t total;
 };
 
@@ -212,6 +212,7 @@ Layout make_layout(const msk_config* c, int G) {
   L.qpart = take(msk::kMaxQSlices * NT * Dq * 4);
   L.apart = take((size_t)G * msk::kWaves * msk::kMaxTok * (c->head_dim + 4) * 4);
   L.attn = take(NT * Dq * 2);
+  L.xq = take(NT * H * 2);
   L.logits = take(4 * NT * E * 4);  // router partial sums per k-slice of the pooler
   L.ppart = take(4 * NT * P * 4);
   L.abuf = take(nsel * NT * I * 2);
@@ -442,6 +443,7 @@ msk::Params base_params(msk_handle h, const msk_io* io) {
   p.qpart = reinterpret_cast<float*>(ws + L.qpart);
   p.apart = reinterpret_cast<float*>(ws + L.apart);
   p.attn = reinterpret_cast<uint16_t*>(ws + L.attn);
+  p.xq = reinterpret_cast<uint16_t*>(ws + L.xq);
   p.logits = reinterpret_cast<float*>(ws + L.logits);
   p.ppart = reinterpret_cast<float*>(ws + L.ppart);
   p.abuf = reinterpret_cast<uint16_t*>(ws + L.abuf);

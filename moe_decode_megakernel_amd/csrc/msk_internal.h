@@ -117,6 +117,7 @@ struct Params {
   float* qpart;           // [q_slices][NT][Dq]
   float* apart;           // attention partials
   uint16_t* attn;         // fp16 [NT][Dq] merged attention output
+  uint16_t* xq;           // fp16 [NT][H] next layer's QKV operand fp16(h_out * g), from the unpooler
   float* logits;          // [p_slices][NT][E] router subtree sums per k-slice (no bias)
   float* ppart;           // [p_slices][NT][P]
   uint16_t* abuf;         // f16 [n_sel_max][NT][I]

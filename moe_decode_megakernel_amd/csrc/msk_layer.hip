@@ -405,20 +405,9 @@ __device__ __forceinline__ void fill_x_norm(const Params& p, const float* h, con
   __syncthreads();
 }
 
-// QKV input of the next layer: X = fp16(h * g) (the RMSNorm scale is applied
-// to the projection's output), and inv_rms from the tile partial sums; the
-// partial sums are requested before the fill so both round trips overlap.
-__device__ __forceinline__ void fill_x_qkv(const Params& p, const float* h, const uint16_t* g, const float* ssq,
-                                           Smem& sm) {
-  const SsqLoads L = ssq_issue(p, ssq);
-  fill_x_norm<2 * kFillBatch>(p, h, g, sm, false);
-  ssq_finish(p, L, sm);
-  __syncthreads();
-}
-
 // X = copy of a 16-bit activation matrix src [NT][K] (already fp16).
+template <int B = 2 * kFillBatch>
 __device__ __forceinline__ void fill_x_copy(const uint16_t* src, int K, int NT, Smem& sm) {
-  constexpr int B = 2 * kFillBatch;
   const int K8 = K / 8, total = kMaxTok * K8;
   for (int i0 = threadIdx.x; i0 < total; i0 += B * kThreads) {
     uint4 v[B];
@@ -437,6 +426,17 @@ __device__ __forceinline__ void fill_x_copy(const uint16_t* src, int K, int NT, 
     }
   }
   vm_drain();
+  __syncthreads();
+}
+
+// QKV input of the next layer: X = fp16(h * g), written by the unpooler's
+// epilogue (the RMSNorm scale is applied to the projection's output), copied
+// in one round trip (16 items per thread at H = 4096); inv_rms from the tile
+// partial sums, requested first so both round trips overlap.
+__device__ __forceinline__ void fill_x_qkv(const Params& p, const uint16_t* xq, const float* ssq, Smem& sm) {
+  const SsqLoads L = ssq_issue(p, ssq);
+  fill_x_copy<4 * kFillBatch>(xq, p.H, p.NT, sm);
+  ssq_finish(p, L, sm);
   __syncthreads();
 }
 
@@ -586,6 +586,8 @@ struct EpiArgs {
   float* ssq;        // partial sums of squares (OProj, Unpool)
   float* dbg_k;
   float* dbg_v;
+  uint16_t* xq;        // Unpool: also write fp16(h_out * gq) (the next layer's QKV operand), or NULL
+  const uint16_t* gq;  // its RMSNorm gains (bf16)
 };
 
 template <Epi E>
@@ -627,6 +629,12 @@ __device__ __forceinline__ void dense_epilogue(const Params& p, const EpiArgs& e
     if (tok < NT) {
       h = res + v;
       st_wt(&ea.out[(size_t)tok * p.H + n], h);
+      if (E == Epi::Unpool && ea.xq) {
+        // the next layer's QKV operand: the RMSNorm scale is applied to the
+        // projection's output, so only the gain multiplies here
+        const float x = p.use_norm ? (h * 1.0f) * bf2f(ea.gq[n]) : h;
+        st_wt(&ea.xq[(size_t)tok * p.H + n], f2h(x));
+      }
     }
     float s = sum16(h * h);
     if (row == 0 && tok < NT) st_wt(&ea.ssq[u.tile * NT + tok], s);
@@ -2138,7 +2146,8 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
     const int parts = max(1, (int)gridDim.x / (p.P / 16));
     fill_x_sum(p.accpart, parts, p.P, p.NT, sm);
     mark(kTrUnpoolFill);
-    EpiArgs ea{nullptr, nullptr, p.h1, p.h_out, p.ssq2, nullptr, nullptr};
+    EpiArgs ea{nullptr, nullptr, p.h1, p.h_out, p.ssq2, nullptr, nullptr,
+               (MODE & kModeQkvNext) != 0 ? p.xq : nullptr, p.nxt.g_attn};
     dense_phase<Epi::Unpool>(p, kSchUnpool, p.cur.w_unpool, p.P, p.P, ea, sm, ring);
     if (DEBUG && p.dbg.acc && blockIdx.x == 0) {
       for (int i = threadIdx.x; i < p.NT * p.P; i += kThreads) {
@@ -2155,7 +2164,7 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
     if (!bar_wait_prefetch(bar, sm, [&] { dense_prefetch<Epi::Qkv>(p, kSchQkv, p.nxt.w_qkv, p.H, nullptr, sm, ring); }))
       return;
     mark(kTrUnpoolBar);
-    fill_x_qkv(p, p.h_out, p.nxt.g_attn, p.ssq2, sm);
+    fill_x_qkv(p, p.xq, p.ssq2, sm);
     mark(kTrQkvFill);
     EpiArgs ea{p.nxt.k_cache, p.nxt.v_cache, nullptr, p.qpart, nullptr, nullptr, nullptr};
     dense_phase<Epi::Qkv>(p, kSchQkv, p.nxt.w_qkv, p.H, p.H, ea, sm, ring);
