@@ -184,6 +184,27 @@ def main():
     step_ms = [per_step[i].elapsed_time(per_step[i + 1]) for i in range(args.steps)]
     med_ms = float(np.median(step_ms))
     mean_ms = total_ms / args.steps
+    hot_med_ms = None
+    if w.n_layers == 1:
+        # A single layer touches ~260 MB, about the size of the memory-side
+        # cache, so back-to-back calls find part of it there. The layer is
+        # timed cold: a 1 GiB streaming read runs between calls (outside the
+        # timed interval); the back-to-back median is reported as hot_us.
+        hot_med_ms = med_ms
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            flush.sum()
+            ev_a[i].record(stream)
+            run(args.warmup + i)
+            ev_b[i].record(stream)
+        torch.cuda.synchronize()
+        step_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(args.steps)]
+        med_ms = float(np.median(step_ms))
+        mean_ms = float(np.mean(step_ms))
+        del flush
 
     # algorithmic bytes from the routing each timed step actually took
     ids_h = ids.cpu().numpy()
@@ -226,7 +247,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "launch": "hip graph per step" if args.graph else "eager (62 launches per step)",
+        "launch": ("hip graph per step" if args.graph else f"eager ({w.n_layers} launches per step)") +
+                  (", cold (1 GiB streaming read between calls)" if w.n_layers == 1 else ""),
         "config": {
             "workload": w.name, "layers": w.n_layers, "tokens_per_request": w.T, "requests": w.R,
             "ctx": w.ctx, "windows": "2048 (46 layers) / global (16 layers)" if w.n_layers == 62 else w.windows[0],
@@ -242,6 +264,7 @@ def main():
         "distinct_experts_per_layer": round(float(np.mean(nsel_all)), 2),
         "top14_overlap": round(float(np.mean(overlaps)), 3) if overlaps else None,
         "step_ms_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
+        "hot_us": round(hot_med_ms * 1e3, 2) if hot_med_ms is not None else None,
         "roofline": {
             "bound": "hbm", "kernel": "msk layer_kernel (one launch per layer boundary)",
             "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -250,7 +273,8 @@ def main():
             "bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(avg_launch_us, 2),
         },
     }
-    log(f"[bench] median step {med_ms:.3f} ms, {result['achieved_tbps']} TB/s")
+    log(f"[bench] median step {med_ms:.3f} ms, {result['achieved_tbps']} TB/s"
+        + (f" (cold; back-to-back {hot_med_ms:.3f} ms)" if hot_med_ms is not None else ""))
     if args.trace:
         result["trace"] = trace_breakdown(w, handle, h_in[-1], h_out, msk, torch, np, dev)
 
