@@ -341,13 +341,26 @@ def cpu_baseline(w, args):
         orc.layer_forward(w, lw, w.R, w.T, [w.ctx] * w.R, h, k, v, w.cap, eps=w.eps, stages=False)
         times[l] = time.perf_counter() - t0
         del lw, k, v
+    # the same first sampled layer on one host thread
+    all_threads = orc.threads()
+    l1 = sample_layers[0]
+    lw = synth.layer_weights(w, l1)
+    k, v = synth.kv_cache(w, l1)
+    orc.set_threads(1)
+    t0 = time.perf_counter()
+    orc.layer_forward(w, lw, w.R, w.T, [w.ctx] * w.R, h, k, v, w.cap, eps=w.eps, stages=False)
+    one_core_s = time.perf_counter() - t0
+    orc.set_threads(all_threads)
+    del lw, k, v
     swa = [times[l] for l in sample_layers if w.windows[l] > 0]
     glb = [times[l] for l in sample_layers if w.windows[l] <= 0]
     n_swa = sum(1 for x in w.windows if x > 0)
     n_glb = len(w.windows) - n_swa
     est = (np.mean(swa) if swa else np.mean(glb)) * n_swa + (np.mean(glb) if glb else np.mean(swa)) * n_glb
     return {
-        "value": round(est * 1e6, 1), "unit": "us", "cores": orc.threads(), "kind": "oracle",
+        "value": round(est * 1e6, 1), "unit": "us", "cores": all_threads, "kind": "oracle",
+        "one_core": {"layer": l1, "seconds": round(one_core_s, 3),
+                     "all_cores_seconds": round(times[l1], 3)},
         "sample": (f"layers {sample_layers} of {w.name} timed on the host "
                    f"({', '.join(f'{l}: {times[l]:.2f} s' for l in sample_layers)}), scaled by layer type "
                    f"to {n_swa} sliding-window + {n_glb} global layers; fp64 oracle, OpenMP over outputs"),

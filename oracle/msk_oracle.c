@@ -25,6 +25,14 @@ int32_t orc_threads(void) {
 #endif
 }
 
+void orc_set_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads((int)n);
+#else
+  (void)n;
+#endif
+}
+
 /* bf16, the storage format of the dense (non-expert) layers and of the KV
  * cache (newruntime.com, What happened): value = the fp32 whose high half is b. */
 double orc_bf16_value(uint16_t b) {

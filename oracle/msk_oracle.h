@@ -111,6 +111,8 @@ int32_t orc_layer_forward(const orc_layer* L, int32_t R, int32_t T, const int32_
                           const uint16_t* tree, const double* h_in, uint16_t* k_cache,
                           uint16_t* v_cache, double* h_out, orc_stages* st);
 int32_t orc_threads(void);
+/* Threads of the OpenMP loops (timing only; results do not depend on it). */
+void orc_set_threads(int32_t n);
 void orc_dense_swiglu(const double* x, int32_t nt, const double* wgu, const double* wd,
                       int32_t P, int32_t I, double* y);
 

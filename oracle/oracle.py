@@ -73,6 +73,8 @@ def lib():
         L.orc_layer_forward.restype = c_i32
         L.orc_dense_swiglu.argtypes = [vp, c_i32, vp, vp, c_i32, c_i32, vp]
         L.orc_threads.restype = c_i32
+        L.orc_set_threads.argtypes = [c_i32]
+        L.orc_set_threads.restype = None
         _lib = L
     return _lib
 
@@ -86,6 +88,11 @@ def _p(a):
 
 def threads() -> int:
     return lib().orc_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops (timing only)."""
+    lib().orc_set_threads(int(n))
 
 
 def bf16_value(b: int) -> float:

@@ -210,3 +210,26 @@ def test_act_fp4_expert_path_matches_library_composition():
     # so the change is of the order of the data itself, not of rounding)
     d = np.abs(st["acc"] - st0["acc"]).max() / np.abs(st0["acc"]).max()
     assert 1e-3 < d < 1.0, d
+
+
+def test_layer_result_does_not_depend_on_the_thread_count():
+    """The oracle parallelises over independent outputs only, so one host
+    thread and all of them give the same bits (the bench times both)."""
+    w = synth.WORKLOADS["tiny_swa"]
+    lw = synth.layer_weights(w, 0)
+    k, v = synth.kv_cache(w, 0)
+    h = synth.h_input(w, 0).astype(np.float64)
+    n = orc.threads()
+    outs = []
+    try:
+        for t in (1, max(2, n)):
+            orc.set_threads(t)
+            kk, vv = k.copy(), v.copy()
+            out, st = orc.layer_forward(w, lw, w.R, w.T, [w.ctx] * w.R, h, kk, vv, w.cap, eps=w.eps)
+            outs.append((out, st["ids"].copy(), kk, vv))
+    finally:
+        orc.set_threads(n)
+    (o1, i1, k1, v1), (o2, i2, k2, v2) = outs
+    assert np.array_equal(o1, o2)
+    assert np.array_equal(i1, i2)
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
