@@ -10,9 +10,11 @@ Decisions against the oracle's own activations: the pre-quantization SwiGLU
 outputs agree within the float tolerance, and a code (or a block scale) may
 differ from the oracle's only where the rounding threshold between the two
 codes lies between the oracle's and the kernel's input value. Such a flip
-moves one value by a whole grid step, so the quantized expert sum is not
-within the max-error bound of a continuous function; it is checked by its
-RMS error, and the layer output by the max-error bound."""
+moves one value by a whole grid step, so the quantized expert sum and the
+layer output are discontinuous in the activations and no max-error bound
+holds for them (measured 1.5e-2 .. 3.4e-2 of the RMS on the layer output
+over seeds); they are gated by their RMS error, and by staying far below
+the quantization's own effect."""
 import numpy as np
 import pytest
 
@@ -25,10 +27,13 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-2  # max |err| <= TOL * RMS(reference), fp32 accumulation on both sides
 
 
-def _inputs(w):
-    lw = synth.layer_weights(w, 0)
-    k, v = synth.kv_cache(w, 0)
-    h = synth.h_input(w, 0)
+def _inputs(w, layer=0, step=0):
+    if layer >= len(w.windows):  # another layer's weights under this workload's window
+        from dataclasses import replace
+        w = replace(w, windows=tuple(w.windows) * (layer + 1))
+    lw = synth.layer_weights(w, layer)
+    k, v = synth.kv_cache(w, layer)
+    h = synth.h_input(w, step)
     return lw, k, v, h
 
 
@@ -55,16 +60,17 @@ def _rms_rel(got, ref):
 
 
 def _check_layer(w, g, o, o_plain, label):
-    errs = {k: rel_err(g[k], o[k]) for k in ("p", "h_out")}
-    acc_max = rel_err(g["acc"], o["acc"])
-    acc_rms = _rms_rel(g["acc"], o["acc"])
+    p_err = rel_err(g["p"], o["p"])  # before the quantization: continuous
+    acc_max, acc_rms = rel_err(g["acc"], o["acc"]), _rms_rel(g["acc"], o["acc"])
+    h_max, h_rms = rel_err(g["h_out"], o["h_out"]), _rms_rel(g["h_out"], o["h_out"])
     # the quantization's own effect, for scale: oracle with vs without it
     effect = _rms_rel(o["acc"], o_plain["acc"])
-    say(f"[{label}] rel errs " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) +
-        f" acc max={acc_max:.2e} rms={acc_rms:.2e}; oracle fp4-vs-unquantized acc rms {effect:.2e}")
-    for k, e in errs.items():
-        assert e <= TOL, (label, k, e)
+    h_effect = _rms_rel(o["h_out"], o_plain["h_out"])
+    say(f"[{label}] p={p_err:.2e} acc max={acc_max:.2e} rms={acc_rms:.2e} h_out max={h_max:.2e} rms={h_rms:.2e}; "
+        f"oracle fp4-vs-unquantized rms: acc {effect:.2e}, h_out {h_effect:.2e}")
+    assert p_err <= TOL, (label, "p", p_err)
     assert acc_rms <= ACC_RMS_TOL, (label, "acc rms", acc_rms)
+    assert h_rms <= TOL, (label, "h_out rms", h_rms)
     # the kernel follows the quantized oracle far more closely than the
     # quantization moves the result
     assert acc_rms < 0.25 * effect, (label, acc_rms, effect)
@@ -164,23 +170,24 @@ def test_act_fp4_off_is_unchanged_and_on_is_deterministic():
     assert not np.array_equal(q1["h_out"], plain["h_out"]), "the flag changed nothing"
 
 
-def test_working_size_act_fp4_layer():
-    w = synth.WORKLOADS["swa_layer"]
-    say("[swa-fp4] generating inputs")
-    lw, k, v, h = _inputs(w)
-    say("[swa-fp4] oracle runs")
+@pytest.mark.parametrize("name,layer,step", [("swa_layer", 0, 0), ("global_layer", 2, 5)])
+def test_working_size_act_fp4_layer(name, layer, step):
+    w = synth.WORKLOADS[name]
+    say(f"[{name}-fp4] generating inputs")
+    lw, k, v, h = _inputs(w, layer, step)
+    say(f"[{name}-fp4] oracle runs")
     o = oracle_layer(w, lw, k, v, h, act_fp4=True)
     o_plain = oracle_layer(w, lw, k, v, h)
     e = int(o["ids"][0, 0])
-    say(f"[swa-fp4] gpu run, dumped expert {e}")
+    say(f"[{name}-fp4] gpu run, dumped expert {e}")
     run = GpuLayerRun(w, lw, k, v, h, flags=msk.MSK_FLAG_ACT_FP4, dq_expert=e)
     g = run.run()
     run.close()
-    _check_quant_dump(w, g, e, "swa-fp4")
+    _check_quant_dump(w, g, e, f"{name}-fp4")
     xo = _oracle_act(w, lw, o, e)
-    say(f"[swa-fp4] act rel err {rel_err(g['act'], xo):.2e}")
+    say(f"[{name}-fp4] act rel err {rel_err(g['act'], xo):.2e}")
     assert rel_err(g["act"], xo) <= TOL
-    _, n_sc, n_code = _check_decisions(w, g, xo, e, "swa-fp4")
+    _, n_sc, n_code = _check_decisions(w, g, xo, e, f"{name}-fp4")
     assert n_sc + n_code <= 0.01 * w.NT * w.I, "more flips than the activation error explains"
     assert np.array_equal(np.sort(g["ids"], axis=1), np.sort(o["ids"], axis=1)), "selection differs"
-    _check_layer(w, g, o, o_plain, "swa-fp4")
+    _check_layer(w, g, o, o_plain, f"{name}-fp4")
