@@ -912,26 +912,35 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
     if (c == 0) trace_stamp(trace_row, kTrAttnKv);
     if (!active || c >= nchunks) continue;
     const int kb = it.k_begin + c * kAttnChunk;
-    // scores for 4 key tiles of 16
+    // scores for 4 key tiles of 16: the K reads and MFMAs of all four tiles
+    // first (independent accumulators, each summed over s in order), then the
+    // mask, evaluated without short-circuit branches. A mask between the
+    // tiles splits the code into blocks the scheduler cannot overlap, and the
+    // tiles then pay their LDS and MFMA latencies one after the other.
+    f32x4_t s4v[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) s4v[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const uint4 a = *reinterpret_cast<const uint4*>(Ks + (kt * 16 + r_) * RS + s * 32 + g_ * 8);
+        s4v[kt] = mfma_f16(a, qb[s], s4v[kt]);
+      }
     float sc[4][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        uint4 a = *reinterpret_cast<const uint4*>(Ks + (kt * 16 + r_) * RS + s * 32 + g_ * 8);
-        s4 = mfma_f16(a, qb[s], s4);
-      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int key = kb + kt * 16 + 4 * g_ + i;
+        const int key = kb + kt * 16 + 4 * g_ + i;
         // prior rows by the window from the token's path position; new rows
         // of its ancestors whose path position is inside the window
         const int u = key - ctx;
-        const int kpos = key < ctx ? key : ctx + (int)((tdepth >> (4 * (u & 15))) & 15u);
-        bool vis = key < it.k_end && r_ < p.T && (key < ctx || ((tanc >> (u & 15)) & 1u)) &&
-                   (window <= 0 || kpos > tpos - window);
-        sc[kt][i] = vis ? s4[i] * scale_log2 : -INFINITY;
+        const bool prior = key < ctx;
+        const int kpos = prior ? key : ctx + (int)((tdepth >> (4 * (u & 15))) & 15u);
+        const bool vis = (key < it.k_end) & (r_ < p.T) & (prior | (((tanc >> (u & 15)) & 1u) != 0u)) &
+                         ((window <= 0) | (kpos > tpos - window));
+        sc[kt][i] = vis ? s4v[kt][i] * scale_log2 : -INFINITY;
       }
     }
     float cmax = -INFINITY;
