@@ -1077,8 +1077,9 @@ __device__ __forceinline__ void merge_phase(const Params& p, const LayerW& lw) {
 // ---------------------------------------------------------------------------
 // WIDE: the slice has at least 512 elements (K8 >= 64), so every wave holds
 // 64 consecutive partials of one token per step and the token index and tree
-// width are wave-uniform.
-template <bool WIDE>
+// width are wave-uniform. RB: tokens whose router tree sums run back to back
+// (the sums and their order are the same for every RB).
+template <bool WIDE, int RB>
 __device__ __forceinline__ void fill_x_pool_router(const Params& p, Smem& sm) {
   const int S = p.p_slices, G = gridDim.x, NT = p.NT, E = p.E;
   const int slice = (int)blockIdx.x % S;
@@ -1128,39 +1129,62 @@ __device__ __forceinline__ void fill_x_pool_router(const Params& p, Smem& sm) {
   __syncthreads();
   for (int it0 = 0; it0 < nit; it0 += B) {
    if (it0 > 0) load_batch(it0);
+   // Per token: normalise, write the fp16 tile, and run the router's fma
+   // chains; then the lane tree sums of RB tokens back to back (independent
+   // chains the scheduler can overlap, which branches between tokens would
+   // prevent), and the sums are stored last. Tokens past NT are zero.
+   static_assert(B % RB == 0, "token batch");
 #pragma unroll
-   for (int q = 0; q < B; ++q) {
-    const int it = it0 + q;
-    if (it >= nit) break;
-    const int t = t_base + it * tstep;
-    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    uint4 out = make_uint4(0, 0, 0, 0);
-    if (t < NT) {
-      const float4 a = ha[q], b = hb[q];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-      const float inv = sm.inv_rms[t];
-      if (p.use_norm) {
+   for (int q0 = 0; q0 < B; q0 += RB) {
+    float racc[RB][kMaxRouterPerWg];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = (v[j] * inv) * gv[j];
-      }
-      out.x = pack2(f2h(v[0]), f2h(v[1]));
-      out.y = pack2(f2h(v[2]), f2h(v[3]));
-      out.z = pack2(f2h(v[4]), f2h(v[5]));
-      out.w = pack2(f2h(v[6]), f2h(v[7]));
+    for (int qq = 0; qq < RB; ++qq) {
+     const int q = q0 + qq;
+     const int it = it0 + q;
+     const int t = t_base + it * tstep;
+     const bool live = it < nit && t < NT;
+     const float4 a = ha[q], b = hb[q];
+     float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+     if (p.use_norm) {
+       const float inv = sm.inv_rms[min(t, kMaxTok - 1)];
+#pragma unroll
+       for (int j = 0; j < 8; ++j) v[j] = (v[j] * inv) * gv[j];
+     }
+#pragma unroll
+     for (int j = 0; j < 8; ++j) v[j] = live ? v[j] : 0.0f;
+     uint4 out;
+     out.x = pack2(f2h(v[0]), f2h(v[1]));
+     out.y = pack2(f2h(v[2]), f2h(v[3]));
+     out.z = pack2(f2h(v[4]), f2h(v[5]));
+     out.w = pack2(f2h(v[6]), f2h(v[7]));
+     if (it < nit && t < kMaxTok) *reinterpret_cast<uint4*>(sm.x + t * x_stride(p.H) + (k0 + j8 * 8) * 2) = out;
+#pragma unroll
+     for (int m = 0; m < kMaxRouterPerWg; ++m) {
+       float acc = 0.0f;
+#pragma unroll
+       for (int j = 0; j < 8; ++j) acc = fmaf(v[j], wv[m][j], acc);
+       racc[qq][m] = acc;
+     }
     }
-    if (t < kMaxTok) *reinterpret_cast<uint4*>(sm.x + t * x_stride(p.H) + (k0 + j8 * 8) * 2) = out;
 #pragma unroll
-    for (int m = 0; m < kMaxRouterPerWg; ++m) {
-      if (m >= n_re) break;
-      float acc = 0.0f;
+    for (int qq = 0; qq < RB; ++qq)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc = fmaf(v[j], wv[m][j], acc);
-      acc = WIDE ? lane_tree_sum(acc, 64) : lane_tree_sum(acc, inwave);
-      if (K8 <= 64) {
-        if (j8 == 0 && t < NT) st_wt(&p.logits[((size_t)slice * NT + t) * E + ev[m]], acc);
-      } else if (lane == 0 && t < kMaxTok) {
-        blk[(t * kMaxRouterPerWg + m) * 8 + j8 / 64] = acc;
-      }
+     for (int m = 0; m < kMaxRouterPerWg; ++m)
+       racc[qq][m] = WIDE ? lane_tree_sum(racc[qq][m], 64) : lane_tree_sum(racc[qq][m], inwave);
+#pragma unroll
+    for (int qq = 0; qq < RB; ++qq) {
+     const int it = it0 + q0 + qq;
+     if (it >= nit) break;
+     const int t = t_base + it * tstep;
+#pragma unroll
+     for (int m = 0; m < kMaxRouterPerWg; ++m) {
+       if (m >= n_re) break;
+       if (K8 <= 64) {
+         if (j8 == 0 && t < NT) st_wt(&p.logits[((size_t)slice * NT + t) * E + ev[m]], racc[qq][m]);
+       } else if (lane == 0 && t < kMaxTok) {
+         blk[(t * kMaxRouterPerWg + m) * 8 + j8 / 64] = racc[qq][m];
+       }
+     }
     }
    }
   }
@@ -2099,8 +2123,10 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
 
   // router + pooler (both read n2 = RMSNorm(h1))
   {
-    if (p.H >= 512 * p.p_slices) fill_x_pool_router<true>(p, sm);
-    else fill_x_pool_router<false>(p, sm);
+    // the stage-dump variant has no registers to spare for batched sums
+    constexpr int RB = DEBUG ? 1 : 4;
+    if (p.H >= 512 * p.p_slices) fill_x_pool_router<true, RB>(p, sm);
+    else fill_x_pool_router<false, RB>(p, sm);
     mark(kTrPoolFill);
     if (DEBUG && p.dbg.n2 && blockIdx.x == 0) dump_n2(p, sm);
     EpiArgs ea{nullptr, nullptr, nullptr, p.ppart, nullptr, nullptr, nullptr};

@@ -56,6 +56,25 @@ def _check_stages(w, g, o, label, window=None):
     return errs
 
 
+def _check_router_bits(w, lw, g, label):
+    """Router logits bit for bit (Tier B): the kernel's fp32 logit of token t
+    and expert e equals the oracle's fixed-order fp32 dot of the kernel's own
+    router input n2[t] with row e, plus the bias (one fp32 add)."""
+    wr = np.ascontiguousarray(lw["w_router"], np.float32)
+    b = lw["b_router"]
+    n2 = np.ascontiguousarray(g["n2"], np.float32)
+    bad = 0
+    for t in range(w.NT):
+        for e in range(w.E):
+            ref = orc.dot_canon_f32(n2[t], wr[e])
+            if b is not None:
+                ref = np.float32(ref + np.float32(b[e]))
+            if np.float32(g["logits"][t, e]).view(np.uint32) != np.float32(ref).view(np.uint32):
+                bad += 1
+    say(f"[{label}] router logits bit-exact: {w.NT * w.E - bad}/{w.NT * w.E}")
+    assert bad == 0, (label, bad)
+
+
 def _check_routing(w, g, o, label):
     # Selection given identical inputs (bit-exact): the kernel's ranked ids
     # and gates from its own fp32 logits equal the oracle's top-k and gates
@@ -82,6 +101,7 @@ def test_tiny_layer_matches_oracle_stage_by_stage():
     o = oracle_layer(w, lw, k, v, h)
     _check_stages(w, g, o, "tiny")
     _check_routing(w, g, o, "tiny")
+    _check_router_bits(w, lw, g, "tiny")
     # KV placement: rows outside [ctx, ctx+T) untouched; written rows are bf16 of the new K/V
     rows = np.ones(w.cap, bool)
     rows[w.ctx:w.ctx + w.T] = False
@@ -134,6 +154,7 @@ def test_working_size_layer_matches_oracle(name, layer, step):
     o = oracle_layer(w, lw, k, v, h)
     _check_stages(w, g, o, name, window=int(lw["window"]))
     _check_routing(w, g, o, name)
+    _check_router_bits(w, lw, g, name)
     n_sel = len(np.unique(o["ids"]))
     say(f"[{name}] distinct experts {n_sel}")
 
