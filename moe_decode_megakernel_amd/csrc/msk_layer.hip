@@ -339,15 +339,23 @@ __device__ __forceinline__ void ssq_finish(const Params& p, const SsqLoads& L, S
     if (threadIdx.x < kMaxTok) sm.inv_rms[threadIdx.x] = 1.0f;
     return;
   }
+  // both tokens' exchange chains first (independent), then the stores
+  float s[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    s[r] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[r] += (lane + q * 64 < nt) ? L.v[r][q] : 0.0f;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) s[r] += __shfl_xor(s[r], o);
+  }
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int t = w + r * kWaves;
-    float s = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (lane + q * 64 < nt) s += L.v[r][q];
-    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-    if (lane == 0 && t < NT) sm.inv_rms[t] = rsqrtf(s / (float)p.H + p.eps);
+    if (lane == 0 && t < NT) sm.inv_rms[t] = rsqrtf(s[r] / (float)p.H + p.eps);
   }
 }
 
