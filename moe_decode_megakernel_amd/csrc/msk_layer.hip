@@ -175,6 +175,43 @@ __device__ __forceinline__ float dpp_f32(float v) {
 __device__ __forceinline__ float readlane_f32(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
+// Combination with the lane 16 or 32 apart by the gfx950 lane swaps
+// (v_permlane16_swap: odd 16-lane rows of the first operand with even rows of
+// the second; v_permlane32_swap: upper half of the first with lower half of
+// the second). Both operands are v, so in every lane the two results are v and
+// its partner's v, in an order that depends on the lane: a commutative
+// combination of the pair equals the combination with the partner. The two
+// results are copied to named words before the bit cast: a bit cast applied
+// to the builtin's second element directly compiles to its first.
+template <int DIST>
+__device__ __forceinline__ void lane_pair(float v, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  uint32_t r0, r1;
+  if constexpr (DIST == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    static_assert(DIST == 32, "distance 16 or 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+template <int DIST>
+__device__ __forceinline__ float max_with_partner(float v) {
+  float a, b;
+  lane_pair<DIST>(v, a, b);
+  return fmaxf(a, b);
+}
+template <int DIST>
+__device__ __forceinline__ float sum_with_partner(float v) {
+  float a, b;
+  lane_pair<DIST>(v, a, b);
+  return a + b;
+}
 __device__ __forceinline__ float lane_tree_sum(float acc, int n) {
   if (n >= 2) acc = acc + dpp_f32<0xB1>(acc);   // quad_perm [1,0,3,2]
   if (n >= 4) acc = acc + dpp_f32<0x4E>(acc);   // quad_perm [2,3,0,1]
@@ -956,8 +993,8 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, sc[kt][i]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    cmax = max_with_partner<16>(cmax);
+    cmax = max_with_partner<32>(cmax);
     const float m_new = fmaxf(m_run, cmax);
     const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
     float psum = 0.0f;
@@ -970,8 +1007,8 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
         psum += pv;
         pb[kt][i] = f2h(pv);
       }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = sum_with_partner<16>(psum);
+    psum = sum_with_partner<32>(psum);
     l_run = l_run * alpha + psum;
     m_run = m_new;
 #pragma unroll
