@@ -15,7 +15,8 @@
  *  - Tensor pointers are device pointers owned by the caller. Weights and KV
  *    caches are borrowed by msk_load_layer and must outlive the handle; IO
  *    buffers must stay valid until the enqueued work has finished.
- *  - Every device pointer must be 16-byte aligned (128-bit loads).
+ *  - Every device pointer must be 16-byte aligned (128-bit loads), except
+ *    msk_io.ctx_len and msk_io.tree_mask (4-byte aligned).
  *  - The library allocates no device memory: its scratch space is the
  *    caller's workspace (msk_workspace_bytes). It allocates a few bytes of
  *    pinned host memory per handle for the device error word.
@@ -25,6 +26,13 @@
  *    capture them in a hipGraph. Calls on one handle are not thread-safe.
  *  - Errors are returned as msk_status; nothing throws or aborts across the
  *    ABI. msk_last_error() describes the last failure on a handle.
+ *  - Argument, shape and alignment checks run on the host before any launch.
+ *    What only the device can see (the device-side ctx_len and tree_mask,
+ *    and a spin-wait that exceeded its budget) sets an error word in the
+ *    workspace: the failed call and every later call on the handle then do
+ *    nothing on the device (their outputs are invalid) until the error has
+ *    been reported, by the next call that finds the failed call complete or
+ *    by msk_synchronize.
  *
  * Weight layouts (row-major, [out][in], the input dim contiguous):
  *  w_qkv    bf16 [nq*d + 2*nkv*d][H], rows Q (head-major) | K | V
@@ -63,7 +71,7 @@ typedef enum {
   MSK_E_SHAPE = 2,    /* shapes the kernel does not support */
   MSK_E_ALIGN = 3,    /* pointer not 16-byte aligned */
   MSK_E_STATE = 4,    /* layer not loaded, or handle in a failed state */
-  MSK_E_CAPACITY = 5, /* ctx_len + n_tokens > kv_capacity, or too many tokens */
+  MSK_E_CAPACITY = 5, /* ctx_len + n_tokens > kv_capacity (reported from the device), or workspace too small */
   MSK_E_HIP = 6,      /* a HIP runtime call failed */
   MSK_E_TIMEOUT = 7   /* a kernel wait exceeded its spin budget (reported by the next call) */
 } msk_status;
@@ -144,13 +152,22 @@ typedef struct {
   float* act;           /* fp32 [NT][I] */
   uint8_t* act_codes;   /* [NT][I/2] E2M1, element 2m in the low nibble of byte m */
   uint8_t* act_scales;  /* [NT][I/16] E4M3 block scales */
+  /* With MSK_FLAG_ACT_FP4, the same encoding for every selected expert, by
+   * expert id (rows of experts not selected are left untouched). */
+  uint8_t* act_codes_all;  /* [E][NT][I/2] */
+  uint8_t* act_scales_all; /* [E][NT][I/16] */
 } msk_debug;
 
 typedef struct {
   int32_t n_requests;     /* R, 1 .. max_requests */
   int32_t n_tokens;       /* T tokens per request, 1 .. max_tokens */
-  const int32_t* ctx_len; /* HOST array [R]: prior context length; the tokens
-                             take positions ctx_len[r] .. ctx_len[r] + T - 1 */
+  const int32_t* ctx_len; /* device [R], 4-byte aligned: prior context length; the
+                             tokens' K/V are written at cache rows ctx_len[r] ..
+                             ctx_len[r] + T - 1. Read by the kernels when they run
+                             (a captured graph follows the values at replay time).
+                             0 <= ctx_len[r] and ctx_len[r] + T <= kv_capacity, else
+                             the call does nothing and reports MSK_E_INVALID /
+                             MSK_E_CAPACITY later (see Conventions). */
   const float* h_in;      /* device fp32 [R*T][H] */
   float* h_out;           /* device fp32 [R*T][H] */
   int32_t* expert_ids;    /* device, may be NULL: [L][R*T][k] (verify_layer: [R*T][k]) */
@@ -165,8 +182,8 @@ typedef struct {
                              100 MHz real-time counter, written by lane 0 of each
                              workgroup at the phase boundaries below; slots a launch
                              does not reach are left untouched. Exclusive with debug. */
-  const uint16_t* tree_mask; /* HOST, may be NULL (= the causal chain): [R][T] ancestor
-                             bitmasks of the verify tokens. The tokens of a request
+  const uint16_t* tree_mask; /* device, may be NULL (= the causal chain), 4-byte
+                             aligned: [R][T] ancestor bitmasks of the verify tokens. The tokens of a request
                              form a tree of candidates (orcarouter.ai, "Muse Spark
                              Open: 1.109 token al secondo ...", section "Anche il
                              modello draft e' diventato piu' veloce ..."). Bit u of
@@ -176,7 +193,12 @@ typedef struct {
                              is ctx_len + depth, depth = ancestors other than t: the
                              window covers the last `window` tokens of its own
                              sequence (prior context, then its path). K/V are still
-                             written at ctx_len + t. Read at enqueue time. */
+                             written at ctx_len + t. Read by the kernels when they
+                             run; an invalid mask makes the call do nothing and
+                             report MSK_E_INVALID later. */
+  float* layer_out;       /* device, may be NULL: [L][R*T][H] the residual leaving each
+                             layer of the call (msk_verify_layer: [1][R*T][H]); the
+                             last entry equals h_out. */
 } msk_io;
 
 /* Trace slots, in execution order ("_BAR" = after the grid barrier that
@@ -217,6 +239,13 @@ msk_status msk_verify_layer(msk_handle h, int32_t layer, const msk_io* io, void*
  * also runs layer 0's QKV and KV write first. expert_ids/gates, if given,
  * receive every layer's routing. */
 msk_status msk_verify_step(msk_handle h, const msk_io* io, void* stream);
+
+/* Waits until the last call enqueued on h (outside graph capture) has
+ * finished and returns the device status of the calls made so far: MSK_OK,
+ * or the first error the device recorded (MSK_E_INVALID, MSK_E_CAPACITY,
+ * MSK_E_TIMEOUT), which it reports once. Outputs of a call that failed on the
+ * device, and of the calls after it until the report, are invalid. */
+msk_status msk_synchronize(msk_handle h);
 
 /* Release the handle (the workspace stays the caller's). */
 msk_status msk_destroy(msk_handle h);

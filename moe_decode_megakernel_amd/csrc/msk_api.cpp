@@ -18,7 +18,7 @@ namespace {
 using msk::kMaxGrid;
 
 struct Layout {
-  size_t bar, err, zeros, sched, h1, ssq1, ssq2, hbuf0, hbuf1, qpart, apart, attn, xq, logits, ppart, abuf, accpart, hist;
+  size_t bar, err, zeros, sched, h1, ssq1, ssq2, hbuf0, hbuf1, qpart, apart, attn, logits, ppart, abuf, accpart, hist;
   size_t total;
 };
 
@@ -137,7 +137,10 @@ struct msk_handle_s {
   int q_slices = 1, p_slices = 1;
   const msk::Unit* wg_units = nullptr;
   const int32_t* wg_nunits = nullptr;
-  int32_t* err_host = nullptr;
+  int32_t* err_host = nullptr;    // pinned copy of the device error word, written at the end of each call
+  hipEvent_t done = nullptr;      // recorded after that copy (calls not under graph capture)
+  bool done_pending = false;      // `done` recorded and not yet observed complete
+  bool clear_err = false;         // the next call's reset zeroes the device error word
   uint64_t calls = 0;  // verify calls enqueued (selects the histogram buffers)
   std::string last_error;
 };
@@ -212,7 +215,6 @@ Layout make_layout(const msk_config* c, int G) {
   L.qpart = take(msk::kMaxQSlices * NT * Dq * 4);
   L.apart = take((size_t)G * msk::kWaves * msk::kMaxTok * (c->head_dim + 4) * 4);
   L.attn = take(NT * Dq * 2);
-  L.xq = take(NT * H * 2);
   L.logits = take(4 * NT * E * 4);  // router partial sums per k-slice of the pooler
   L.ppart = take(4 * NT * P * 4);
   L.abuf = take(nsel * NT * I * 2);
@@ -243,6 +245,13 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
   const int G = std::min(prop.multiProcessorCount, kMaxGrid);
   if (cfg->n_experts > msk::kMaxRouterPerWg * G)
     return fail(nullptr, MSK_E_SHAPE, "n_experts exceeds the router rows the workgroups of one launch cover");
+  // attention runs at least one work item per (request, kv head) and the
+  // launch has one workgroup per compute unit
+  if ((int64_t)cfg->max_requests * cfg->n_kv_heads > G)
+    return fail(nullptr, MSK_E_SHAPE, "max_requests * n_kv_heads exceeds the compute units of the device");
+  // the grid barrier needs every workgroup resident at once
+  if (msk_layer_min_occupancy() < 1)
+    return fail(nullptr, MSK_E_SHAPE, "the layer kernel does not fit one workgroup per compute unit on this device");
   {
     // GEMM1 stages 256 B per (selected expert, 8-row i-tile) unit of a workgroup in LDS
     const int64_t nsel = std::min<int64_t>(cfg->n_experts, (int64_t)pass_tokens(cfg) * cfg->top_k);
@@ -327,6 +336,11 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
     return fail(nullptr, MSK_E_HIP, "hipHostMalloc of the error word failed");
   }
   *h->err_host = 0;
+  if (hipEventCreateWithFlags(&h->done, hipEventDisableTiming) != hipSuccess) {
+    (void)hipHostFree(h->err_host);
+    delete h;
+    return fail(nullptr, MSK_E_HIP, "hipEventCreate failed");
+  }
   *out = h;
   return MSK_OK;
 }
@@ -372,43 +386,54 @@ msk::LayerW to_w(const msk_layer_desc& d) {
   return w;
 }
 
-msk_status check_io(msk_handle h, const msk_io* io) {
+// Device status of completed calls: the error word a call copied back once
+// its event shows the copy landed (or when no eager call is pending, a copy
+// made by a graph replay). A nonzero word is reported once; the device word
+// stays set (every later launch does nothing) until the next call's reset
+// clears it.
+msk_status poll_device_status(msk_handle h, bool wait) {
+  if (h->done_pending) {
+    hipError_t q = wait ? hipEventSynchronize(h->done) : hipEventQuery(h->done);
+    if (q == hipErrorNotReady) return MSK_OK;
+    if (q != hipSuccess) return fail(h, MSK_E_HIP, std::string("waiting for the previous call failed: ") + hipGetErrorString(q));
+    h->done_pending = false;
+  }
+  const int32_t e = __atomic_load_n(h->err_host, __ATOMIC_ACQUIRE);
+  if (e == 0) return MSK_OK;
+  __atomic_store_n(h->err_host, 0, __ATOMIC_RELEASE);
+  h->clear_err = true;
+  if (e == MSK_E_INVALID)
+    return fail(h, MSK_E_INVALID, "a previous call was given an invalid ctx_len or tree_mask (its outputs are invalid)");
+  if (e == MSK_E_CAPACITY)
+    return fail(h, MSK_E_CAPACITY, "a previous call had ctx_len + n_tokens > kv_capacity (its outputs are invalid)");
+  char buf[128];
+  snprintf(buf, sizeof buf, "a previous call reported device error %d (spin budget exceeded; its outputs are invalid)", e);
+  return fail(h, MSK_E_TIMEOUT, buf);
+}
+
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+msk_status check_io(msk_handle h, const msk_io* io, hipStream_t s) {
   if (!io) return fail(h, MSK_E_INVALID, "io is NULL");
   const msk_config& c = h->cfg;
   if (io->n_requests < 1 || io->n_requests > c.max_requests) return fail(h, MSK_E_INVALID, "n_requests out of range");
   if (io->n_tokens < 1 || io->n_tokens > c.max_tokens) return fail(h, MSK_E_INVALID, "n_tokens out of range");
   if (!io->ctx_len) return fail(h, MSK_E_INVALID, "ctx_len is NULL");
-  for (int r = 0; r < io->n_requests; ++r) {
-    if (io->ctx_len[r] < 0) return fail(h, MSK_E_INVALID, "ctx_len must be >= 0");
-    if ((int64_t)io->ctx_len[r] + io->n_tokens > c.kv_capacity) return fail(h, MSK_E_CAPACITY, "ctx_len + n_tokens exceeds kv_capacity");
-  }
+  if (!aligned4(io->ctx_len)) return fail(h, MSK_E_ALIGN, "ctx_len must be 4-byte aligned");
+  if (io->tree_mask && !aligned4(io->tree_mask)) return fail(h, MSK_E_ALIGN, "tree_mask must be 4-byte aligned");
   if (!io->h_in || !io->h_out) return fail(h, MSK_E_INVALID, "h_in and h_out are required");
   if (!aligned16(io->h_in) || !aligned16(io->h_out)) return fail(h, MSK_E_ALIGN, "h_in/h_out must be 16-byte aligned");
+  if (io->layer_out && !aligned16(io->layer_out)) return fail(h, MSK_E_ALIGN, "layer_out must be 16-byte aligned");
   if (io->debug && io->trace) return fail(h, MSK_E_INVALID, "debug dumps and the trace are exclusive");
   if (io->trace && !aligned16(io->trace)) return fail(h, MSK_E_ALIGN, "trace must be 16-byte aligned");
   if ((io->expert_ids && !aligned16(io->expert_ids)) || (io->gates && !aligned16(io->gates)))
     return fail(h, MSK_E_ALIGN, "expert_ids/gates must be 16-byte aligned");
   if (io->prefetch_ids && !aligned16(io->prefetch_ids)) return fail(h, MSK_E_ALIGN, "prefetch_ids must be 16-byte aligned");
-  if (io->tree_mask) {
-    const int T = io->n_tokens;
-    for (int r = 0; r < io->n_requests; ++r)
-      for (int t = 0; t < T; ++t) {
-        const uint32_t a = io->tree_mask[r * T + t];
-        if (!((a >> t) & 1u) || (a >> (t + 1)) != 0u)
-          return fail(h, MSK_E_INVALID, "tree_mask: a token's mask must hold itself and no later token");
-        for (int u = 0; u < t; ++u)
-          if (((a >> u) & 1u) && (io->tree_mask[r * T + u] & ~a) != 0u)
-            return fail(h, MSK_E_INVALID, "tree_mask: a token's mask must hold its ancestors' masks");
-      }
-  }
-  if (*h->err_host != 0) {
-    int e = *h->err_host;
-    *h->err_host = 0;
-    char buf[96];
-    snprintf(buf, sizeof buf, "a previous launch reported device error %d (spin budget exceeded)", e);
-    return fail(h, MSK_E_TIMEOUT, buf);
-  }
-  return MSK_OK;
+  // no event query while the stream is being captured (not permitted there)
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return fail(h, MSK_E_HIP, "hipStreamIsCapturing failed");
+  if (cs != hipStreamCaptureStatusNone) return MSK_OK;
+  return poll_device_status(h, false);
 }
 
 msk::Params base_params(msk_handle h, const msk_io* io) {
@@ -431,7 +456,9 @@ msk::Params base_params(msk_handle h, const msk_io* io) {
   p.use_norm = (c.flags & MSK_FLAG_NO_NORM) ? 0 : 1;
   p.act_fp4 = (c.flags & MSK_FLAG_ACT_FP4) ? 1 : 0;
   p.eps = c.rms_eps;
-  for (int r = 0; r < io->n_requests; ++r) p.ctx[r] = io->ctx_len[r];
+  p.ctx_dev = io->ctx_len;
+  p.tree_dev = io->tree_mask;
+  p.r0 = 0;
   p.q_slices = h->q_slices;
   p.p_slices = h->p_slices;
   uint8_t* ws = h->ws;
@@ -443,7 +470,6 @@ msk::Params base_params(msk_handle h, const msk_io* io) {
   p.qpart = reinterpret_cast<float*>(ws + L.qpart);
   p.apart = reinterpret_cast<float*>(ws + L.apart);
   p.attn = reinterpret_cast<uint16_t*>(ws + L.attn);
-  p.xq = reinterpret_cast<uint16_t*>(ws + L.xq);
   p.logits = reinterpret_cast<float*>(ws + L.logits);
   p.ppart = reinterpret_cast<float*>(ws + L.ppart);
   p.abuf = reinterpret_cast<uint16_t*>(ws + L.abuf);
@@ -473,6 +499,12 @@ msk_status finish(msk_handle h, hipStream_t s) {
   const Layout& L = h->lay;
   if (hipMemcpyAsync(h->err_host, h->ws + L.err, 4, hipMemcpyDeviceToHost, s) != hipSuccess)
     return fail(h, MSK_E_HIP, "hipMemcpyAsync of the error word failed");
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return fail(h, MSK_E_HIP, "hipStreamIsCapturing failed");
+  if (cs == hipStreamCaptureStatusNone) {
+    if (hipEventRecord(h->done, s) != hipSuccess) return fail(h, MSK_E_HIP, "hipEventRecord failed");
+    h->done_pending = true;
+  }
   return MSK_OK;
 }
 
@@ -504,9 +536,15 @@ msk_status run_call(msk_handle h, int l0, int l1, const msk_io* io, hipStream_t 
   if ((io->debug || io->trace) && R > rpp)
     return fail(h, MSK_E_INVALID, "debug dumps and the trace need all tokens of the call in one 16-token pass");
   float* hb[2] = {reinterpret_cast<float*>(h->ws + L.hbuf0), reinterpret_cast<float*>(h->ws + L.hbuf1)};
-  if (msk_launch_reset(reinterpret_cast<uint32_t*>(h->ws + L.bar), reinterpret_cast<int32_t*>(h->ws + L.err), s) !=
-      hipSuccess)
+  // residual leaving launch i of pass r0 (the last launch writes h_out)
+  auto resid = [&](int i, int r0) -> float* {
+    if (io->layer_out) return io->layer_out + (size_t)i * NT_all * H + (size_t)r0 * T * H;
+    return hb[i & 1];
+  };
+  if (msk_launch_reset(reinterpret_cast<uint32_t*>(h->ws + L.bar), reinterpret_cast<int32_t*>(h->ws + L.err),
+                       h->clear_err, s) != hipSuccess)
     return fail(h, MSK_E_HIP, "reset launch failed");
+  h->clear_err = false;
   uint32_t base = 0;
   for (int r0 = 0; r0 < R; r0 += rpp) {
     const int nr = std::min(rpp, R - r0);
@@ -515,25 +553,14 @@ msk_status run_call(msk_handle h, int l0, int l1, const msk_io* io, hipStream_t 
       msk::Params p = base_params(h, io);
       p.R = nr;
       p.NT = nr * T;
-      for (int r = 0; r < msk::kMaxReq; ++r) p.ctx[r] = r < nr ? io->ctx_len[r0 + r] : 0;
-      for (int r = 0; r < msk::kMaxReq; ++r) {
-        uint64_t dp = 0;
-        for (int t = 0; t < msk::kMaxTok; ++t) {
-          uint32_t a = 0;
-          if (r < nr && t < T) a = io->tree_mask ? io->tree_mask[(r0 + r) * T + t] : ((2u << t) - 1u);
-          p.tree[r][t] = (uint16_t)a;
-          const uint64_t depth = a ? (uint64_t)(__builtin_popcount(a) - 1) : 0u;
-          dp |= depth << (4 * t);
-        }
-        p.tree_depth[r] = dp;
-      }
+      p.r0 = r0;
       p.mode = (i == 0 ? msk::kModeQkvOwn : 0u) | (i + 1 < n ? msk::kModeQkvNext : 0u);
       p.layer = l;
       p.bar_base = base;
       p.cur = layer_for_pass(h->layers[l], r0, c);
       p.nxt = (i + 1 < n) ? layer_for_pass(h->layers[l + 1], r0, c) : p.cur;
-      p.h_in = (i == 0) ? io->h_in + (size_t)r0 * T * H : hb[(i - 1) & 1];
-      p.h_out = (i == n - 1) ? io->h_out + (size_t)r0 * T * H : hb[i & 1];
+      p.h_in = (i == 0) ? io->h_in + (size_t)r0 * T * H : resid(i - 1, r0);
+      p.h_out = (i == n - 1) ? io->h_out + (size_t)r0 * T * H : resid(i, r0);
       const size_t row0 = (size_t)i * NT_all * K + (size_t)r0 * T * K;
       p.out_ids = io->expert_ids ? io->expert_ids + row0 : nullptr;
       p.out_gates = io->gates ? io->gates + row0 : nullptr;
@@ -546,13 +573,18 @@ msk_status run_call(msk_handle h, int l0, int l1, const msk_io* io, hipStream_t 
       if (debug) {
         const msk_debug& d = *io->debug;
         p.dbg = msk::Debug{d.q, d.k_new, d.v_new, d.attn, d.h1, d.n2, d.logits, d.p, d.acc,
-                           d.dq_expert, d.dq_gate_up, d.dq_down, d.act, d.act_codes, d.act_scales};
+                           d.dq_expert, d.dq_gate_up, d.dq_down, d.act, d.act_codes, d.act_scales,
+                           d.act_codes_all, d.act_scales_all};
       }
       hipError_t e = msk_launch_layer(p, h->grid, debug, s);
       if (e != hipSuccess) return fail(h, MSK_E_HIP, std::string("layer launch failed: ") + hipGetErrorString(e));
       base += barriers_of(p.mode);
     }
   }
+  if (io->layer_out &&
+      hipMemcpyAsync(io->layer_out + (size_t)(n - 1) * NT_all * H, io->h_out, (size_t)NT_all * H * sizeof(float),
+                     hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return fail(h, MSK_E_HIP, "hipMemcpyAsync of the last layer's residual failed");
   h->calls += 1;
   return finish(h, s);
 }
@@ -563,7 +595,7 @@ extern "C" msk_status msk_verify_layer(msk_handle h, int32_t layer, const msk_io
   if (!h) return fail(nullptr, MSK_E_INVALID, "handle is NULL");
   if (layer < 0 || layer >= h->cfg.n_layers) return fail(h, MSK_E_INVALID, "layer out of range");
   if (!h->loaded[layer]) return fail(h, MSK_E_STATE, "layer not loaded");
-  msk_status st = check_io(h, io);
+  msk_status st = check_io(h, io, (hipStream_t)stream);
   if (st != MSK_OK) return st;
   return run_call(h, layer, layer + 1, io, (hipStream_t)stream, io->debug != nullptr);
 }
@@ -572,14 +604,20 @@ extern "C" msk_status msk_verify_step(msk_handle h, const msk_io* io, void* stre
   if (!h) return fail(nullptr, MSK_E_INVALID, "handle is NULL");
   for (int l = 0; l < h->cfg.n_layers; ++l)
     if (!h->loaded[l]) return fail(h, MSK_E_STATE, "not every layer is loaded");
-  msk_status st = check_io(h, io);
+  msk_status st = check_io(h, io, (hipStream_t)stream);
   if (st != MSK_OK) return st;
   if (io->debug) return fail(h, MSK_E_INVALID, "debug dumps are honoured by msk_verify_layer only");
   return run_call(h, 0, h->cfg.n_layers, io, (hipStream_t)stream, false);
 }
 
+extern "C" msk_status msk_synchronize(msk_handle h) {
+  if (!h) return fail(nullptr, MSK_E_INVALID, "handle is NULL");
+  return poll_device_status(h, true);
+}
+
 extern "C" msk_status msk_destroy(msk_handle h) {
   if (!h) return fail(nullptr, MSK_E_INVALID, "handle is NULL");
+  if (h->done) (void)hipEventDestroy(h->done);
   if (h->err_host) (void)hipHostFree(h->err_host);
   delete h;
   return MSK_OK;

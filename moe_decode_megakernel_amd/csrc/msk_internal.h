@@ -83,6 +83,8 @@ struct Debug {
   float* act;         // [NT][I] SwiGLU output of dq_expert before activation quantization
   uint8_t* act_codes; // [NT][I/2] its E2M1 codes
   uint8_t* act_sc;    // [NT][I/16] its E4M3 block scales
+  uint8_t* act_codes_all; // [E][NT][I/2] E2M1 codes of every selected expert (by expert id)
+  uint8_t* act_sc_all;    // [E][NT][I/16] their block scales
 };
 
 // Schedules of the dense phases, built once per handle and stored per
@@ -98,9 +100,12 @@ struct Params {
   int32_t use_norm;
   int32_t act_fp4;        // SwiGLU outputs quantized to NVFP4 before the down projection
   float eps;
-  int32_t ctx[kMaxReq];
-  uint16_t tree[kMaxReq][kMaxTok];  // ancestor bitmask of each verify token (self included)
-  uint64_t tree_depth[kMaxReq];     // 4 bits per token: its number of ancestors
+  // Request metadata in device memory, read by every workgroup at launch
+  // start: prior context lengths ctx_dev[r0 + r] and, unless tree_dev is
+  // NULL (the causal chain), the ancestor bitmasks tree_dev[(r0 + r)*T + t].
+  const int32_t* ctx_dev;
+  const uint16_t* tree_dev;
+  int32_t r0;             // first request of this launch's pass
   int32_t q_slices, p_slices;
   uint32_t mode;
   int32_t layer;          // layer whose attention .. unpooler this launch runs
@@ -117,7 +122,6 @@ struct Params {
   float* qpart;           // [q_slices][NT][Dq]
   float* apart;           // attention partials
   uint16_t* attn;         // fp16 [NT][Dq] merged attention output
-  uint16_t* xq;           // fp16 [NT][H] next layer's QKV operand fp16(h_out * g), from the unpooler
   float* logits;          // [p_slices][NT][E] router subtree sums per k-slice (no bias)
   float* ppart;           // [p_slices][NT][P]
   uint16_t* abuf;         // f16 [n_sel_max][NT][I]
@@ -143,4 +147,7 @@ struct Params {
 // Launchers implemented in msk_layer.hip.
 hipError_t msk_launch_layer(const msk::Params& p, int grid, bool debug, hipStream_t s);
 hipError_t msk_launch_pack_down_scale(const uint8_t* src, uint8_t* dst, int E, int P, int I, hipStream_t s);
-hipError_t msk_launch_reset(uint32_t* bar, int32_t* err, hipStream_t s);
+hipError_t msk_launch_reset(uint32_t* bar, int32_t* err, bool clear_err, hipStream_t s);
+// Fewest layer-kernel workgroups of kThreads that one compute unit can hold,
+// over the kernel's instantiations (the grid must be co-resident).
+int msk_layer_min_occupancy();

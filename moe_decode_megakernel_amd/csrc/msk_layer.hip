@@ -49,6 +49,12 @@ struct Smem {
   int32_t nunits[kSchCount];
   int32_t plist[kMaxPrefetch];          // speculative expert prefetch list
   int32_t flag;
+  // request metadata of the launch (read from device memory at launch start)
+  int32_t ctx[kMaxReq];                 // prior context length per request of the pass
+  uint32_t tanc[kMaxReq][kMaxTok];      // ancestor bitmask per verify token (self included)
+  uint64_t tdepth[kMaxReq];             // 4 bits per token: its number of ancestors
+  int32_t io_code;                      // 0, or the error code of invalid metadata
+  int32_t err0;                         // device error word at launch start
 };
 
 __device__ __forceinline__ f32x4_t mfma_f16(uint4 a, uint4 b, f32x4_t c) {
@@ -117,33 +123,20 @@ __device__ __forceinline__ void ring_fence() { __builtin_amdgcn_sched_barrier(0)
 // from that loop alone.
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// ctx[r] without a dynamic index into the kernel argument (which would be a
-// vector load from the argument segment inside a ring loop).
-__device__ __forceinline__ int ctx_of(const Params& p, int r) {
-  int c = __builtin_amdgcn_readfirstlane(p.ctx[0]);
-#pragma unroll
-  for (int i = 1; i < kMaxReq; ++i) c = (r == i) ? __builtin_amdgcn_readfirstlane(p.ctx[i]) : c;
-  return c;
-}
+// Prior context length of request r of the pass (from LDS; the caller takes
+// readfirstlane where r is wave-uniform).
+__device__ __forceinline__ int ctx_of(const Smem& sm, int r) { return sm.ctx[r]; }
+__device__ __forceinline__ int ctx_uni(const Smem& sm, int r) { return __builtin_amdgcn_readfirstlane(sm.ctx[r]); }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // Verify-token tree of request r (wave-uniform) seen from token t (per lane):
 // t's ancestor bitmask, and the packed depths of all the request's tokens.
-// Selects over the kernel-argument tables keep the reads scalar.
-__device__ __forceinline__ uint32_t tree_anc_of(const Params& p, int r, int t) {
-  uint32_t a = 0;
-#pragma unroll
-  for (int rr = 0; rr < kMaxReq; ++rr)
-#pragma unroll
-    for (int u = 0; u < kMaxTok; ++u) a = (r == rr && t == u) ? (uint32_t)p.tree[rr][u] : a;
-  return a;
-}
-__device__ __forceinline__ uint64_t tree_depth_of(const Params& p, int r) {
-  uint64_t d = p.tree_depth[0];
-#pragma unroll
-  for (int rr = 1; rr < kMaxReq; ++rr) d = (r == rr) ? p.tree_depth[rr] : d;
-  return d;
+__device__ __forceinline__ uint32_t tree_anc_of(const Smem& sm, int r, int t) { return sm.tanc[r][t]; }
+__device__ __forceinline__ uint64_t tree_depth_of(const Smem& sm, int r) {
+  const uint64_t d = sm.tdepth[r];
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(d >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)d);
 }
 
 // Phase-boundary slots of the self-timing trace (one uint64 per slot, per
@@ -396,16 +389,17 @@ __device__ __forceinline__ void ssq_finish(const Params& p, const SsqLoads& L, S
   }
 }
 
-// X = fp16(h * inv_rms * g), or fp16(h * g) when the caller applies inv_rms to
-// the projection's output instead (with_inv = false), or fp16(h) without the
-// norm; rounded to nearest even. Item i = (token i / K8, elements 8*(i % K8)
+// X = fp16(h * inv_rms * g), or fp16(h) without the norm; rounded to nearest
+// even. The normalised value is bounded by sqrt(H) * |g| (no element of a
+// vector exceeds sqrt(n) times its RMS), so a residual of any magnitude stays
+// inside fp16's range once the RMS scale is applied, and the scale is applied
+// before the rounding. Item i = (token i / K8, elements 8*(i % K8)
 // .. +8); a thread's items share one k range (K8 divides the workgroup
 // size), and the loads of kFillBatch items are issued before any is used.
 constexpr int kFillBatch = 4;
 
 template <int B = kFillBatch>
-__device__ __forceinline__ void fill_x_norm(const Params& p, const float* h, const uint16_t* g, Smem& sm,
-                                            bool with_inv = true) {
+__device__ __forceinline__ void fill_x_norm(const Params& p, const float* h, const uint16_t* g, Smem& sm) {
   const int K = p.H, NT = p.NT, K8 = K / 8;
   const int total = kMaxTok * K8;
   const int k = (threadIdx.x % K8) * 8;
@@ -433,7 +427,7 @@ __device__ __forceinline__ void fill_x_norm(const Params& p, const float* h, con
       uint4 out = make_uint4(0, 0, 0, 0);
       if (t < NT) {
         float v[8] = {a[q].x, a[q].y, a[q].z, a[q].w, b[q].x, b[q].y, b[q].z, b[q].w};
-        const float inv = with_inv ? sm.inv_rms[t] : 1.0f;
+        const float inv = sm.inv_rms[t];
         if (p.use_norm) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] = (v[j] * inv) * gj[j];
@@ -474,14 +468,61 @@ __device__ __forceinline__ void fill_x_copy(const uint16_t* src, int K, int NT, 
   __syncthreads();
 }
 
-// QKV input of the next layer: X = fp16(h * g), written by the unpooler's
-// epilogue (the RMSNorm scale is applied to the projection's output), copied
-// in one round trip (16 items per thread at H = 4096); inv_rms from the tile
-// partial sums, requested first so both round trips overlap.
-__device__ __forceinline__ void fill_x_qkv(const Params& p, const uint16_t* xq, const float* ssq, Smem& sm) {
+// QKV input of the next layer: X = fp16(h * inv_rms * g) from the fp32
+// residual the unpooler wrote, with inv_rms from the unpooler's per-tile
+// partial sums of squares. The partial sums and the first half of the
+// residual are requested together (one round trip), the second half after.
+__device__ __forceinline__ void fill_x_qkv(const Params& p, const float* h, const float* ssq, const uint16_t* g,
+                                           Smem& sm) {
+  constexpr int B = 2 * kFillBatch;
+  const int K = p.H, NT = p.NT, K8 = K / 8;
+  const int total = kMaxTok * K8;
+  const int k = (threadIdx.x % K8) * 8;
   const SsqLoads L = ssq_issue(p, ssq);
-  fill_x_copy<4 * kFillBatch>(xq, p.H, p.NT, sm);
-  ssq_finish(p, L, sm);
+  float gj[8];
+  {
+    const uint4 gg = *reinterpret_cast<const uint4*>(g + k);
+    const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gj[j] = p.use_norm ? bf2f((uint16_t)(gw[j >> 1] >> ((j & 1) * 16))) : 1.0f;
+  }
+  bool first = true;
+  for (int i0 = threadIdx.x; i0 < total; i0 += B * kThreads) {
+    float4 a[B], b[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const int t = min((i0 + q * kThreads) / K8, NT - 1);
+      const float4* hp = reinterpret_cast<const float4*>(h + (size_t)t * K + k);
+      a[q] = hp[0];
+      b[q] = hp[1];
+    }
+    if (first) {
+      ssq_finish(p, L, sm);
+      __syncthreads();
+      first = false;
+    }
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const int i = i0 + q * kThreads;
+      if (i >= total) break;
+      const int t = i / K8;
+      uint4 out = make_uint4(0, 0, 0, 0);
+      if (t < NT) {
+        float v[8] = {a[q].x, a[q].y, a[q].z, a[q].w, b[q].x, b[q].y, b[q].z, b[q].w};
+        if (p.use_norm) {
+          const float inv = sm.inv_rms[t];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = (v[j] * inv) * gj[j];
+        }
+        out.x = pack2(f2h(v[0]), f2h(v[1]));
+        out.y = pack2(f2h(v[2]), f2h(v[3]));
+        out.z = pack2(f2h(v[4]), f2h(v[5]));
+        out.w = pack2(f2h(v[6]), f2h(v[7]));
+      }
+      *reinterpret_cast<uint4*>(sm.x + t * x_stride(K) + k * 2) = out;
+    }
+  }
+  vm_drain();
   __syncthreads();
 }
 
@@ -631,8 +672,6 @@ struct EpiArgs {
   float* ssq;        // partial sums of squares (OProj, Unpool)
   float* dbg_k;
   float* dbg_v;
-  uint16_t* xq;        // Unpool: also write fp16(h_out * gq) (the next layer's QKV operand), or NULL
-  const uint16_t* gq;  // its RMSNorm gains (bf16)
 };
 
 template <Epi E>
@@ -647,7 +686,6 @@ __device__ __forceinline__ void dense_epilogue(const Params& p, const EpiArgs& e
   if constexpr (E == Epi::Qkv) {
     const int Dq = p.nq * p.d, Dkv = p.nkv * p.d;
     if (tok < NT) {
-      v *= sm.inv_rms[tok];
       if (n < Dq) {
         st_wt(&ea.out[((size_t)(u.slot & kUnitSlotMask) * NT + tok) * Dq + n], v);
       } else {
@@ -656,7 +694,7 @@ __device__ __forceinline__ void dense_epilogue(const Params& p, const EpiArgs& e
         if (is_v) c -= Dkv;
         int g = c / p.d, cc = c % p.d;
         int r = tok / p.T, t = tok % p.T;
-        size_t dst = (((size_t)r * p.nkv + g) * p.cap + ctx_of(p, r) + t) * p.d + cc;
+        size_t dst = (((size_t)r * p.nkv + g) * p.cap + ctx_of(sm, r) + t) * p.d + cc;
         if (is_v) {
           st_wt(&ea.v_cache[dst], f2bf(v));
           if (ea.dbg_v) ea.dbg_v[(size_t)tok * Dkv + c] = v;
@@ -674,12 +712,6 @@ __device__ __forceinline__ void dense_epilogue(const Params& p, const EpiArgs& e
     if (tok < NT) {
       h = res + v;
       st_wt(&ea.out[(size_t)tok * p.H + n], h);
-      if (E == Epi::Unpool && ea.xq) {
-        // the next layer's QKV operand: the RMSNorm scale is applied to the
-        // projection's output, so only the gain multiplies here
-        const float x = p.use_norm ? (h * 1.0f) * bf2f(ea.gq[n]) : h;
-        st_wt(&ea.xq[(size_t)tok * p.H + n], f2h(x));
-      }
     }
     float s = sum16(h * h);
     if (row == 0 && tok < NT) st_wt(&ea.ssq[u.tile * NT + tok], s);
@@ -748,8 +780,9 @@ struct AttnItem {
   int r, g, s, nsplit, k_begin, k_end;  // keys [k_begin, k_end)
 };
 
-__device__ __forceinline__ void attn_range(const Params& p, const LayerW& lw, int r, int& lo, int& hi) {
-  const int ctx = ctx_of(p, r);
+__device__ __forceinline__ void attn_range(const Params& p, const Smem& sm, const LayerW& lw, int r, int& lo,
+                                           int& hi) {
+  const int ctx = ctx_uni(sm, r);
   lo = (lw.window > 0) ? max(0, ctx - lw.window + 1) : 0;
   hi = ctx + p.T - 1;
 }
@@ -768,10 +801,11 @@ __device__ __forceinline__ int attn_splits(const Params& p, int nkeys, int grid)
 }
 
 // Item of a flat index; returns false if idx is past the last item.
-__device__ __forceinline__ bool attn_item(const Params& p, const LayerW& lw, int idx, int grid, AttnItem& it) {
+__device__ __forceinline__ bool attn_item(const Params& p, const Smem& sm, const LayerW& lw, int idx, int grid,
+                                          AttnItem& it) {
   for (int r = 0; r < p.R; ++r) {
     int lo, hi;
-    attn_range(p, lw, r, lo, hi);
+    attn_range(p, sm, lw, r, lo, hi);
     int nk = hi - lo + 1;
     int S = attn_splits(p, nk, grid);
     int n_r = S * p.nkv;
@@ -791,11 +825,12 @@ __device__ __forceinline__ bool attn_item(const Params& p, const LayerW& lw, int
 }
 
 // Index of the first item of (r, g) in the flat order.
-__device__ __forceinline__ int attn_item_base(const Params& p, const LayerW& lw, int r, int g, int grid, int& S) {
+__device__ __forceinline__ int attn_item_base(const Params& p, const Smem& sm, const LayerW& lw, int r, int g,
+                                              int grid, int& S) {
   int base = 0;
   for (int rr = 0; rr < p.R; ++rr) {
     int lo, hi;
-    attn_range(p, lw, rr, lo, hi);
+    attn_range(p, sm, lw, rr, lo, hi);
     int s = attn_splits(p, hi - lo + 1, grid);
     if (rr == r) {
       S = s;
@@ -809,11 +844,11 @@ __device__ __forceinline__ int attn_item_base(const Params& p, const LayerW& lw,
 
 // Number of attention items of the launch (workgroups at or past it are idle
 // during the attention phase).
-__device__ __forceinline__ int attn_item_count(const Params& p, const LayerW& lw, int grid) {
+__device__ __forceinline__ int attn_item_count(const Params& p, const Smem& sm, const LayerW& lw, int grid) {
   int n = 0;
   for (int r = 0; r < p.R; ++r) {
     int lo, hi;
-    attn_range(p, lw, r, lo, hi);
+    attn_range(p, sm, lw, r, lo, hi);
     n += attn_splits(p, hi - lo + 1, grid) * p.nkv;
   }
   return n;
@@ -828,17 +863,17 @@ __device__ __forceinline__ float* apart_at(const Params& p, int item, int w, int
 template <int D>
 __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& lw, Smem& sm, uint64_t* trace_row) {
   AttnItem it;
-  if (!attn_item(p, lw, blockIdx.x, gridDim.x, it)) return;
+  if (!attn_item(p, sm, lw, blockIdx.x, gridDim.x, it)) return;
   const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4, w = wave_id();
   const int group = p.nq / p.nkv;
   const int Dq = p.nq * p.d;
   const bool active = w < group;
   const int h = it.g * group + w;
-  const int ctx = ctx_of(p, it.r);
+  const int ctx = ctx_uni(sm, it.r);
   const int window = lw.window;
   // this lane's token: ancestor set and position ctx + depth on its own path
-  const uint32_t tanc = tree_anc_of(p, it.r, min(r_, kMaxTok - 1));
-  const uint64_t tdepth = tree_depth_of(p, it.r);
+  const uint32_t tanc = tree_anc_of(sm, it.r, min(r_, kMaxTok - 1));
+  const uint64_t tdepth = tree_depth_of(sm, it.r);
   const int tpos = ctx + (int)((tdepth >> (4 * min(r_, kMaxTok - 1))) & 15u);
   constexpr int KS = D / 32;     // MFMA steps over the head dim
   constexpr int DT = D / 16;     // d tiles of the PV product
@@ -1055,7 +1090,7 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
 constexpr int kMergeChunk = 16;
 
 template <bool debug>
-__device__ __forceinline__ void merge_phase(const Params& p, const LayerW& lw) {
+__device__ __forceinline__ void merge_phase(const Params& p, const Smem& sm, const LayerW& lw) {
   const int D = p.d, Dq = p.nq * D, group = p.nq / p.nkv;
   const int lane = lane_id(), half = lane >> 5;
   const int qpr = D / 32;
@@ -1067,7 +1102,7 @@ __device__ __forceinline__ void merge_phase(const Params& p, const LayerW& lw) {
     const int r = tok / p.T, t = tok % p.T;
     const int g = h / group, w = h % group;
     int S;
-    const int base = attn_item_base(p, lw, r, g, gridDim.x, S);
+    const int base = attn_item_base(p, sm, lw, r, g, gridDim.x, S);
     const int dim = dq * 32 + (lane & 31);
     const int nper = (S + 1) / 2;  // splits per half-wave (the odd half may have one fewer)
     float2 ml = *reinterpret_cast<const float2*>(apart_at(p, base + min(lane, S - 1), w, t) + D);
@@ -1369,8 +1404,8 @@ __device__ __forceinline__ float route_logit(const RouteLoads& L, int S, int tt,
 // arithmetic of fill_x_sum), items as in fill_x_sum, kSumBatch items per
 // thread per batch (one batch covers K <= 2048). Loads are unconditional
 // (slice and token indices clamped in range).
-constexpr int kSumBatch = 8;
-static_assert(kSumBatch * kThreads >= kMaxTok * 2048 / 8, "one batch covers the pooled tile");
+constexpr int kSumBatch = 4;
+static_assert(2 * kSumBatch * kThreads >= kMaxTok * 2048 / 8, "two batches cover the pooled tile");
 struct SumLoads {
   float4 a[kMaxPSlices][kSumBatch], b[kMaxPSlices][kSumBatch];
 };
@@ -1862,6 +1897,11 @@ __device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
       st_wt16(dst, u32x4_t{hv[0], hv[1], hv[2], hv[3]});
       st_wt16(dst + 8, u32x4_t{hv[4], hv[5], hv[6], hv[7]});
       if constexpr (debug) {
+        if (p.dbg.act_codes_all) {
+          const size_t row = (size_t)rt.sel[j] * NT + tok;
+          *reinterpret_cast<uint2*>(p.dbg.act_codes_all + row * (I / 2) + it * 4) = make_uint2(codes[0], codes[1]);
+          p.dbg.act_sc_all[row * (I / 16) + it / 2] = (uint8_t)sc;
+        }
         if (p.dbg.act && rt.sel[j] == p.dbg.dq_expert) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) p.dbg.act[(size_t)tok * I + it * 8 + i] = x[i];
@@ -2078,6 +2118,69 @@ __device__ __forceinline__ void stage_units(const Params& p, Smem& sm) {
   }
 }
 
+// Device error codes (the numbers of the matching msk_status values).
+constexpr int32_t kErrInvalid = 1;   // a token mask breaks the tree rules, or ctx_len < 0
+constexpr int32_t kErrCapacity = 5;  // ctx_len + n_tokens > kv_capacity
+
+// Request metadata of the launch, from device memory (one round trip,
+// together with the error word and this workgroup's schedule rows): the
+// pass's context lengths and token masks go to LDS, wave 0 checks them and
+// packs the token depths. Every workgroup reads the same words and takes the
+// same decision, so either all of them run the launch or none does. Returns
+// false when the launch must do nothing: an earlier launch failed (the error
+// word is sticky until the host has read it) or the metadata is invalid
+// (workgroup 0 then records the error code).
+//   ctx: 0 <= ctx, ctx + T <= cap.
+//   masks: bit t set, no bit above t, and each ancestor's mask contained in
+//   the token's own (the tree rules of the causal verify pass).
+__device__ __forceinline__ bool load_request_meta(const Params& p, Smem& sm) {
+  const int tid = threadIdx.x;
+  if (tid < p.R) sm.ctx[tid] = p.ctx_dev[p.r0 + tid];
+  if (tid < kMaxReq * kMaxTok) {
+    const int r = tid / kMaxTok, t = tid % kMaxTok;
+    uint32_t a = 0;
+    if (r < p.R && t < p.T) a = p.tree_dev ? (uint32_t)p.tree_dev[(size_t)(p.r0 + r) * p.T + t] : ((2u << t) - 1u);
+    sm.tanc[r][t] = a;
+  }
+  if (tid == 0) sm.err0 = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (wave_id() == 0) {
+    const int lane = lane_id(), r = lane / kMaxTok, t = lane % kMaxTok;
+    const bool live = r < p.R && t < p.T;
+    const uint32_t a = sm.tanc[r][t];
+    bool ok = true;
+    if (live) {
+      ok = ((a >> t) & 1u) != 0u && (a >> (t + 1)) == 0u;
+      for (int u = 0; u < kMaxTok; ++u)
+        if (u < t && ((a >> u) & 1u) != 0u && (sm.tanc[r][u] & ~a) != 0u) ok = false;
+    }
+    const uint64_t dep = live ? (uint64_t)(__builtin_popcount(a) - 1) << (4 * t) : 0ull;
+    int code = __ballot(!ok) != 0ull ? kErrInvalid : 0;
+    if (lane < p.R) {
+      const int c = sm.ctx[lane];
+      if (c < 0) ok = false;
+    }
+    if (__ballot(!ok) != 0ull) code = kErrInvalid;
+    if (code == 0) {
+      const bool cap_ok = lane >= p.R || (int64_t)sm.ctx[lane] + p.T <= (int64_t)p.cap;
+      if (__ballot(!cap_ok) != 0ull) code = kErrCapacity;
+    }
+    // depths of request r: the OR of its 16 lanes' fields (lanes 16r .. 16r+15)
+    uint64_t pk = dep;
+#pragma unroll
+    for (int o = 1; o < kMaxTok; o <<= 1) pk |= (uint64_t)__shfl_xor((long long)pk, o);
+    if (t == 0) sm.tdepth[r] = pk;
+    if (lane == 0) sm.io_code = code;
+  }
+  __syncthreads();
+  if (sm.err0 != 0) return false;
+  if (sm.io_code != 0) {
+    if (blockIdx.x == 0 && tid == 0) __hip_atomic_store(p.err, sm.io_code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+  }
+  return true;
+}
+
 template <uint32_t MODE, int VARIANT>
 __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   constexpr bool DEBUG = VARIANT == kDebug;
@@ -2096,12 +2199,12 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   DenseSlot ring[kRing];
   if (threadIdx.x == 0) sm.zero = make_uint4(0, 0, 0, 0);
   stage_units(p, sm);
-  if constexpr ((MODE & kModeQkvOwn) != 0) __syncthreads();
+  if (!load_request_meta(p, sm)) return;
 
   if constexpr ((MODE & kModeQkvOwn) != 0) {
     dense_prefetch<Epi::Qkv>(p, kSchQkv, p.cur.w_qkv, p.H, nullptr, sm, ring);
     compute_inv_rms(p, p.h_in, nullptr, sm);
-    fill_x_norm(p, p.h_in, p.cur.g_attn, sm, false);
+    fill_x_norm(p, p.h_in, p.cur.g_attn, sm);
     EpiArgs ea{p.cur.k_cache, p.cur.v_cache, nullptr, p.qpart, nullptr, DEBUG ? p.dbg.k_new : nullptr,
                DEBUG ? p.dbg.v_new : nullptr};
     dense_phase<Epi::Qkv>(p, kSchQkv, p.cur.w_qkv, p.H, p.H, ea, sm, ring);
@@ -2122,7 +2225,7 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   // attention of the launch's layer. Workgroups without an attention item
   // publish nothing in this phase: with a speculative prefetch they arrive at
   // the barrier first and read the listed experts while the others attend.
-  const int n_items = p.n_prefetch > 0 ? attn_item_count(p, p.cur, gridDim.x) : (int)gridDim.x;
+  const int n_items = p.n_prefetch > 0 ? attn_item_count(p, sm, p.cur, gridDim.x) : (int)gridDim.x;
   if ((int)blockIdx.x >= n_items) {
     bar_arrive(bar);
     prefetch_rank(p, sm);
@@ -2143,7 +2246,7 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   if (!bar_wait(bar, sm)) return;
   mark(kTrAttnBar);
 
-  merge_phase<DEBUG>(p, p.cur);
+  merge_phase<DEBUG>(p, sm, p.cur);
   mark(kTrMerge);
   bar_arrive(bar);
   if (!bar_wait_prefetch(bar, sm, [&] { dense_prefetch<Epi::OProj>(p, kSchOproj, p.cur.w_o, Dq, p.h_in, sm, ring); }))
@@ -2226,8 +2329,7 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
     const int parts = max(1, (int)gridDim.x / (p.P / 16));
     fill_x_sum(p.accpart, parts, p.P, p.NT, sm);
     mark(kTrUnpoolFill);
-    EpiArgs ea{nullptr, nullptr, p.h1, p.h_out, p.ssq2, nullptr, nullptr,
-               (MODE & kModeQkvNext) != 0 ? p.xq : nullptr, p.nxt.g_attn};
+    EpiArgs ea{nullptr, nullptr, p.h1, p.h_out, p.ssq2, nullptr, nullptr};
     dense_phase<Epi::Unpool>(p, kSchUnpool, p.cur.w_unpool, p.P, p.P, ea, sm, ring);
     if (DEBUG && p.dbg.acc && blockIdx.x == 0) {
       for (int i = threadIdx.x; i < p.NT * p.P; i += kThreads) {
@@ -2244,7 +2346,7 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
     if (!bar_wait_prefetch(bar, sm, [&] { dense_prefetch<Epi::Qkv>(p, kSchQkv, p.nxt.w_qkv, p.H, nullptr, sm, ring); }))
       return;
     mark(kTrUnpoolBar);
-    fill_x_qkv(p, p.xq, p.ssq2, sm);
+    fill_x_qkv(p, p.h_out, p.ssq2, p.nxt.g_attn, sm);
     mark(kTrQkvFill);
     EpiArgs ea{p.nxt.k_cache, p.nxt.v_cache, nullptr, p.qpart, nullptr, nullptr, nullptr};
     dense_phase<Epi::Qkv>(p, kSchQkv, p.nxt.w_qkv, p.H, p.H, ea, sm, ring);
@@ -2252,9 +2354,12 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   }
 }
 
-__global__ void reset_kernel(uint32_t* bar, int32_t* err) {
+// Start of a call: zero the barrier flags; the error word only when the
+// host has read the error it holds (it stays set until then, so every later
+// launch does nothing).
+__global__ void reset_kernel(uint32_t* bar, int32_t* err, int32_t clear_err) {
   if (threadIdx.x < kMaxGrid) bar[threadIdx.x] = 0;
-  if (threadIdx.x == 0) *err = 0;
+  if (threadIdx.x == 0 && clear_err) *err = 0;
 }
 
 }  // namespace
@@ -2314,7 +2419,27 @@ hipError_t msk_launch_pack_down_scale(const uint8_t* src, uint8_t* dst, int E, i
   return hipGetLastError();
 }
 
-hipError_t msk_launch_reset(uint32_t* bar, int32_t* err, hipStream_t s) {
-  hipLaunchKernelGGL(msk::reset_kernel, dim3(1), dim3(msk::kMaxGrid), 0, s, bar, err);
+hipError_t msk_launch_reset(uint32_t* bar, int32_t* err, bool clear_err, hipStream_t s) {
+  hipLaunchKernelGGL(msk::reset_kernel, dim3(1), dim3(msk::kMaxGrid), 0, s, bar, err, clear_err ? 1 : 0);
   return hipGetLastError();
+}
+
+template <uint32_t MODE, int V>
+static int occupancy_of() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, msk::layer_kernel<MODE, V>, msk::kThreads, 0) != hipSuccess)
+    return 0;
+  return n;
+}
+
+int msk_layer_min_occupancy() {
+  using namespace msk;
+  const int v[] = {occupancy_of<kModeQkvOwn, kPlain>(), occupancy_of<kModeQkvOwn | kModeQkvNext, kPlain>(),
+                   occupancy_of<kModeQkvNext, kPlain>(), occupancy_of<0u, kPlain>(),
+                   occupancy_of<kModeQkvOwn, kTrace>(), occupancy_of<kModeQkvOwn | kModeQkvNext, kTrace>(),
+                   occupancy_of<kModeQkvNext, kTrace>(), occupancy_of<0u, kTrace>(),
+                   occupancy_of<kModeQkvOwn, kDebug>()};
+  int m = v[0];
+  for (int x : v) m = std::min(m, x);
+  return m;
 }

@@ -18,8 +18,8 @@ MSK_FLAG_NO_NORM = 0x1
 MSK_FLAG_ACT_FP4 = 0x2
 
 EXPORTS = ("msk_workspace_bytes", "msk_create", "msk_load_layer", "msk_verify_layer",
-           "msk_verify_step", "msk_destroy", "msk_down_scale_bytes", "msk_pack_down_scale",
-           "msk_last_error")
+           "msk_verify_step", "msk_synchronize", "msk_destroy", "msk_down_scale_bytes",
+           "msk_pack_down_scale", "msk_last_error")
 
 
 class msk_config(ctypes.Structure):
@@ -43,14 +43,15 @@ DEBUG_PTRS = ("q", "k_new", "v_new", "attn", "h1", "n2", "logits", "p", "acc")
 
 class msk_debug(ctypes.Structure):
     _fields_ = [(n, vp) for n in DEBUG_PTRS] + [("dq_expert", i32), ("dq_gate_up", vp), ("dq_down", vp),
-                                                ("act", vp), ("act_codes", vp), ("act_scales", vp)]
+                                                ("act", vp), ("act_codes", vp), ("act_scales", vp),
+                                                ("act_codes_all", vp), ("act_scales_all", vp)]
 
 
 class msk_io(ctypes.Structure):
-    _fields_ = [("n_requests", i32), ("n_tokens", i32), ("ctx_len", ctypes.POINTER(i32)),
+    _fields_ = [("n_requests", i32), ("n_tokens", i32), ("ctx_len", vp),
                 ("h_in", vp), ("h_out", vp), ("expert_ids", vp), ("gates", vp),
                 ("debug", ctypes.POINTER(msk_debug)), ("prefetch_ids", vp), ("trace", vp),
-                ("tree_mask", ctypes.POINTER(ctypes.c_uint16))]
+                ("tree_mask", vp), ("layer_out", vp)]
 
 
 TRACE_SLOTS = ["start", "qkv_own", "qkv_own_bar", "attn_q", "attn_kv", "attn", "attn_bar", "merge", "merge_bar", "oproj_fill",
@@ -80,6 +81,8 @@ def lib():
         L.msk_verify_layer.restype = i32
         L.msk_verify_step.argtypes = [vp, ctypes.POINTER(msk_io), vp]
         L.msk_verify_step.restype = i32
+        L.msk_synchronize.argtypes = [vp]
+        L.msk_synchronize.restype = i32
         L.msk_destroy.argtypes = [vp]
         L.msk_destroy.restype = i32
         L.msk_down_scale_bytes.argtypes = [i32, i32, i32]
@@ -121,6 +124,10 @@ def msk_verify_layer(h, layer: int, io: msk_io, stream: int) -> int:
 
 def msk_verify_step(h, io: msk_io, stream: int) -> int:
     return lib().msk_verify_step(h, ctypes.byref(io), vp(stream))
+
+
+def msk_synchronize(h) -> int:
+    return lib().msk_synchronize(h)
 
 
 def msk_destroy(h) -> int:
@@ -167,28 +174,33 @@ def make_layer_desc(t: Dict, window: int) -> msk_layer_desc:
     return d
 
 
-def make_io(n_requests, n_tokens, ctx: Sequence[int], h_in, h_out, expert_ids=None, gates=None,
-            debug: Optional[msk_debug] = None, trace=None, prefetch_ids=None, tree_mask=None):
-    """tree_mask: host array-like [n_requests][n_tokens] of ancestor bitmasks, or None."""
-    ctx_arr = (i32 * len(ctx))(*ctx)
-    tree_arr = None
-    if tree_mask is not None:
+def make_io(n_requests, n_tokens, ctx, h_in, h_out, expert_ids=None, gates=None,
+            debug: Optional[msk_debug] = None, trace=None, prefetch_ids=None, tree_mask=None, layer_out=None):
+    """ctx: device int32 tensor [n_requests], or a host sequence (copied to a
+    device tensor on h_in's device, kept alive by the returned struct).
+    tree_mask: device uint16/int16 tensor [n_requests][n_tokens], a host
+    array-like of ancestor bitmasks (copied likewise), or None (the chain)."""
+    import torch
+    dev = h_in.device
+    if not torch.is_tensor(ctx):
+        ctx = torch.tensor([int(c) for c in ctx], dtype=torch.int32, device=dev)
+    if tree_mask is not None and not torch.is_tensor(tree_mask):
         flat = [int(x) for row in tree_mask for x in (row if hasattr(row, "__len__") else [row])]
         if len(flat) != n_requests * n_tokens:
             raise ValueError("tree_mask needs n_requests * n_tokens entries")
-        tree_arr = (ctypes.c_uint16 * len(flat))(*flat)
-    io = msk_io(n_requests=n_requests, n_tokens=n_tokens, ctx_len=ctypes.cast(ctx_arr, ctypes.POINTER(i32)),
+        tree_mask = torch.tensor([x - 65536 if x >= 32768 else x for x in flat], dtype=torch.int16, device=dev)
+    io = msk_io(n_requests=n_requests, n_tokens=n_tokens, ctx_len=_ptr(ctx),
                 h_in=_ptr(h_in), h_out=_ptr(h_out), expert_ids=_ptr(expert_ids), gates=_ptr(gates),
                 debug=ctypes.pointer(debug) if debug is not None else None, prefetch_ids=_ptr(prefetch_ids),
-                trace=_ptr(trace),
-                tree_mask=ctypes.cast(tree_arr, ctypes.POINTER(ctypes.c_uint16)) if tree_arr is not None else None)
-    io._keep = (ctx_arr, debug, tree_arr)
+                trace=_ptr(trace), tree_mask=_ptr(tree_mask), layer_out=_ptr(layer_out))
+    io._keep = (ctx, debug, tree_mask)
     return io
 
 
 def make_debug(t: Dict, dq_expert: int = -1) -> msk_debug:
     d = msk_debug(dq_expert=dq_expert, dq_gate_up=_ptr(t.get("dq_gate_up")), dq_down=_ptr(t.get("dq_down")),
-                  act=_ptr(t.get("act")), act_codes=_ptr(t.get("act_codes")), act_scales=_ptr(t.get("act_scales")))
+                  act=_ptr(t.get("act")), act_codes=_ptr(t.get("act_codes")), act_scales=_ptr(t.get("act_scales")),
+                  act_codes_all=_ptr(t.get("act_codes_all")), act_scales_all=_ptr(t.get("act_scales_all")))
     for n in DEBUG_PTRS:
         setattr(d, n, _ptr(t.get(n)))
     return d
@@ -247,6 +259,10 @@ class Handle:
         import torch
         s = torch.cuda.current_stream().cuda_stream if stream is None else stream
         self.check(msk_verify_step(self.h, io, s))
+
+    def synchronize(self):
+        """Wait for the last call and raise MskError if the device reported one."""
+        self.check(msk_synchronize(self.h))
 
     def close(self):
         if self.h:

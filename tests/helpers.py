@@ -59,16 +59,22 @@ class GpuLayerRun:
             "act": torch.zeros((NT, w.I), **f32),
             "act_codes": torch.zeros((NT, w.I // 2), dtype=torch.uint8, device=dev),
             "act_scales": torch.zeros((NT, w.I // 16), dtype=torch.uint8, device=dev),
+            "act_codes_all": torch.zeros((w.E, NT, w.I // 2), dtype=torch.uint8, device=dev),
+            "act_scales_all": torch.zeros((w.E, NT, w.I // 16), dtype=torch.uint8, device=dev),
         }
         self.ctx = [w.ctx] * w.R if ctx is None else list(ctx)
         self.dq_expert = dq_expert
 
-    def run(self, debug=True, tree=None):
+    def run(self, debug=True, tree=None, trace=None):
+        """One msk_verify_layer call; debug=False runs the production kernel
+        (the benchmark's variant) with no stage dumps. Device-side errors are
+        raised (msk_synchronize)."""
         torch = self.torch
         d = msk.make_debug(self.dbg, self.dq_expert) if debug else None
         io = msk.make_io(self.w.R, self.w.T, self.ctx, self.h_in, self.h_out, self.ids, self.gates, d,
-                         tree_mask=tree)
+                         tree_mask=tree, trace=trace)
         self.handle.verify_layer(0, io)
+        self.handle.synchronize()
         torch.cuda.synchronize()
         out = {k: v.cpu().numpy() for k, v in self.dbg.items()}
         out["h_out"] = self.h_out.cpu().numpy()
@@ -124,3 +130,48 @@ def routing_mismatches(gpu_ids, logits, k, thr):
 def random_tree(T, seed):
     """Seeded tree of T verify tokens (ancestor bitmasks, self included)."""
     return synth.verify_tree(T, seed)
+
+
+def teacher_forced_layer(w, layer, h_prev, gpu_out, gpu_ids, label, tol=2e-2, route_thr=2e-3, ctx=None):
+    """The oracle's layer `layer` fed the GPU's own input residual h_prev
+    (teacher forcing), against the GPU's output residual of that layer.
+
+    Routing: the GPU's expert set of a token must equal the oracle's wherever
+    the oracle's k-th/(k+1)-th logit margin exceeds route_thr, and ranks
+    closer than route_thr may swap (R20). The output residual is gated at
+    max|err| <= tol * RMS(oracle output) over the tokens whose expert sets
+    agree (a near-tie selection legitimately changes a token's output); at
+    most max(2, NT/16) tokens may be near-ties. Only the experts either side selects
+    are generated. Returns (max error / RMS, error on the layer delta / RMS
+    of the delta, number of near-tie tokens, the oracle's K and V caches
+    after its KV write)."""
+    ctx = [w.ctx] * w.R if ctx is None else list(ctx)
+    need = set(np.unique(gpu_ids).tolist())
+    h64 = np.asarray(h_prev, np.float64)
+    for _ in range(3):
+        lw = synth.layer_weights(w, layer, experts=sorted(need))
+        k, v = synth.kv_cache(w, layer)
+        out, st = orc.layer_forward(w, lw, w.R, w.T, ctx, h64, k, v, w.cap, eps=w.eps)
+        extra = set(np.unique(st["ids"]).tolist()) - need
+        if not extra:
+            break
+        need |= extra
+    else:
+        raise AssertionError(f"{label}: expert sets did not settle")
+    K = w.k
+    bad = routing_mismatches(gpu_ids, st["logits"], K, route_thr)
+    assert not bad, f"{label}: routing differs beyond near-ties for tokens {bad}"
+    same = np.array([set(gpu_ids[t].tolist()) == set(st["ids"][t].tolist()) for t in range(w.NT)])
+    n_tie = int((~same).sum())
+    assert n_tie <= max(2, w.NT // 16), f"{label}: {n_tie} near-tie tokens"
+    ref = np.asarray(out, np.float64)
+    got = np.asarray(gpu_out, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = float(np.max(np.abs(got[same] - ref[same]))) / rms
+    d_ref = ref - h64
+    d_rms = float(np.sqrt(np.mean(d_ref * d_ref)))
+    derr = float(np.max(np.abs((got - h64)[same] - d_ref[same]))) / d_rms
+    say(f"[{label}] layer {layer} (window {w.windows[layer]}): h_out max|err|/RMS {err:.2e}, "
+        f"on the layer delta {derr:.2e}, near-tie tokens {n_tie}, distinct experts {len(np.unique(gpu_ids))}")
+    assert err <= tol, f"{label}: layer {layer} output error {err:.3e} > {tol}"
+    return err, derr, n_tie, k, v

@@ -12,7 +12,7 @@ import pytest
 
 from moe_decode_megakernel_amd import msk, synth
 from oracle import oracle as orc
-from tests.helpers import bf16_to_f64, rel_err, routing_mismatches, say
+from tests.helpers import bf16_to_f64, rel_err, routing_mismatches, say, teacher_forced_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +36,7 @@ def _run_stack(w, ctx, h, dev="cuda"):
     ids = torch.zeros((w.n_layers, w.NT, w.k), dtype=torch.int32, device=dev)
     io = msk.make_io(w.R, w.T, ctx, h_in, h_out, ids)
     handle.verify_step(io)
+    handle.synchronize()
     torch.cuda.synchronize()
     out = h_out.cpu().numpy()
     gids = ids.cpu().numpy()
@@ -70,8 +71,13 @@ def test_tiny_requests_match_joint_oracle(R, T, ctx):
 
 def test_batch4_step62_full_size():
     """4 requests x 16 tokens through the 62-layer stack at working size,
-    65536-token caches per request, uniform routing: the oracle's joint chain
-    over the first two layers, and run-to-run identity of the whole step."""
+    65536-token caches per request, uniform routing. Each layer's output
+    residual is returned (msk_io.layer_out); the oracle runs layers 0
+    (sliding window, first launch), 3 (global, middle launch) and 61 (global,
+    last launch) teacher-forced on the GPU's input residual of that layer, all
+    four requests jointly (attention per request, MoE over the 64 tokens), and
+    each output is gated at max|err| <= 2e-2 * RMS. A repeated step gives
+    identical bytes."""
     import torch
     w = synth.WORKLOADS["batch4_step62"]
     dev = "cuda"
@@ -85,40 +91,30 @@ def test_batch4_step62_full_size():
     h = synth.h_input(w, 0)
     h_in = torch.from_numpy(np.ascontiguousarray(h, np.float32)).to(dev)
     L, NT, K = w.n_layers, w.NT, w.k
-    outs, ids_runs = [], []
-    rows = slice(w.ctx, w.ctx + w.T)
-    kv0 = None
+    outs, ids_runs, lo_out = [], [], None
     for run in range(2):
         h_out = torch.zeros_like(h_in)
         ids = torch.zeros((L, NT, K), dtype=torch.int32, device=dev)
-        io = msk.make_io(w.R, w.T, [w.ctx] * w.R, h_in, h_out, ids)
+        lo = torch.zeros((L, NT, w.H), dtype=torch.float32, device=dev) if run == 0 else None
+        io = msk.make_io(w.R, w.T, [w.ctx] * w.R, h_in, h_out, ids, layer_out=lo)
         say(f"[batch4] gpu step, run {run}")
         handle.verify_step(io)
+        handle.synchronize()
         torch.cuda.synchronize()
         outs.append(h_out.cpu().numpy())
         ids_runs.append(ids.cpu().numpy())
-        if kv0 is None:
-            kv0 = [(layers[l]["k_cache"][:, :, rows].cpu().numpy().view(np.uint16),
-                    layers[l]["v_cache"][:, :, rows].cpu().numpy().view(np.uint16)) for l in range(2)]
+        if lo is not None:
+            lo_out = lo.cpu().numpy()
     handle.close()
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(ids_runs[0], ids_runs[1])
-    assert np.all(np.isfinite(outs[0]))
+    assert np.array_equal(lo_out[L - 1], outs[0])
+    assert np.all(np.isfinite(lo_out))
     n_sel = [len(np.unique(ids_runs[0][l])) for l in range(L)]
     say(f"[batch4] distinct experts per layer: mean {np.mean(n_sel):.1f}, min {min(n_sel)}, max {max(n_sel)}")
     del layers
     torch.cuda.empty_cache()
-    hh = h.astype(np.float64)
-    for l in range(2):
-        say(f"[batch4] oracle layer {l}")
-        lw = synth.layer_weights(w, l)
-        k, v = synth.kv_cache(w, l)
-        hh, st = orc.layer_forward(w, lw, w.R, w.T, [w.ctx] * w.R, hh, k, v, w.cap, eps=w.eps)
-        bad = routing_mismatches(ids_runs[0][l], st["logits"], K, 1e-3 if l == 0 else 4e-3)
-        say(f"[batch4] layer {l}: routing mismatches {bad}")
-        assert not bad
-        for name, got, ref in (("K", kv0[l][0], k[:, :, rows]), ("V", kv0[l][1], v[:, :, rows])):
-            g64, r64 = bf16_to_f64(got), bf16_to_f64(ref)
-            rms = float(np.sqrt(np.mean(r64 * r64)))
-            bound = TOL * rms + np.ldexp(1.0, -7) * np.abs(r64)
-            assert float(np.max(np.abs(g64 - r64) - bound)) <= 0.0, f"layer {l}: {name} write"
-        del lw, k, v
+    errs = {}
+    for l in (0, 3, 61):
+        h_prev = h if l == 0 else lo_out[l - 1]
+        errs[l] = teacher_forced_layer(w, l, h_prev, lo_out[l], ids_runs[0][l], "batch4", tol=TOL)[:3]
+    say("[batch4] per-layer h_out error / RMS: " + " ".join(f"{l}:{e[0]:.2e}" for l, e in errs.items()))

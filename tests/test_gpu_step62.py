@@ -1,30 +1,33 @@
 """Full-size parity of the 62-layer verify step (16 tokens, hidden 4096, 46
 sliding-window layers of window 2048 + 16 global layers, 16384-token caches,
 top-8 of 256 NVFP4 experts, Zipf-skewed routing), run exactly as the benchmark
-runs it: one msk_verify_step over 62 resident layer launches.
+runs it: one msk_verify_step over 62 resident layer launches, production
+kernel variants (first, middle and last launch).
 
-The oracle cannot run 62 full layers inside a test, so:
-- the first four layers (three sliding-window, one global) are checked
-  against the oracle's own chain: expert ids exactly where the routing margin
-  is safe, and the K/V rows each layer writes within tolerance;
-- the whole step is checked by properties that hold at any size: a repeated
-  call is bit-identical, every layer's cache rows outside C..C+T-1 are
-  unchanged (sampled), and h_out is finite.
+Each layer's output residual is returned (msk_io.layer_out). The oracle runs
+a set of layers teacher-forced on the GPU's own input residual of that layer
+(layer 0 on the step's input): sliding-window layers 0, 1, 30, 60 and global
+layers 3, 31, 59, 61, covering the first launch (its own QKV projection), the
+middle launches (QKV projected at the previous launch's tail) and the last
+launch. Each is gated at max|err| <= 2e-2 * RMS, with routing checked per R20.
+The whole step is also checked by properties at any size: repeated calls and
+the self-timing variant give identical bytes, cache rows outside the verify
+slots are unchanged, and the K/V rows each checked layer writes agree with
+the oracle's.
 """
 import numpy as np
 import pytest
 
 from moe_decode_megakernel_amd import msk, synth
-from oracle import oracle as orc
-from tests.helpers import bf16_to_f64, rel_err, routing_margins, routing_mismatches, say
+from tests.helpers import bf16_to_f64, say, teacher_forced_layer
 
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
-N_ORACLE_LAYERS = 4
+CHECK_LAYERS = (0, 1, 3, 30, 31, 59, 60, 61)
 
 
-def test_step62_full_size():
+def test_step62_full_size_teacher_forced():
     import torch
     w = synth.WORKLOADS["step62"]
     dev = "cuda"
@@ -39,74 +42,55 @@ def test_step62_full_size():
     h_in = torch.from_numpy(np.ascontiguousarray(h, np.float32)).to(dev)
     L, NT, K = w.n_layers, w.NT, w.k
     rows = slice(w.ctx, w.ctx + w.T)
-    # sampled untouched cache rows: the last history rows and a few spread out
     probe = torch.tensor([0, 1, w.ctx // 2, w.ctx - 2, w.ctx - 1], device=dev)
     before = [(t["k_cache"][:, :, probe].cpu().numpy(), t["v_cache"][:, :, probe].cpu().numpy()) for t in layers]
 
-    outs, ids_runs, kv_runs = [], [], []
-    for run in range(2):
+    runs = []
+    for run, mode in enumerate(("layer_out", "plain", "trace")):
         h_out = torch.zeros_like(h_in)
         ids = torch.zeros((L, NT, K), dtype=torch.int32, device=dev)
-        gates = torch.zeros((L, NT, K), dtype=torch.float32, device=dev)
-        io = msk.make_io(w.R, w.T, [w.ctx] * w.R, h_in, h_out, ids, gates)
-        say(f"[step62] gpu step, run {run}")
+        lo = torch.zeros((L, NT, w.H), dtype=torch.float32, device=dev) if mode == "layer_out" else None
+        tr = torch.zeros((L, msk.MAX_GRID, len(msk.TRACE_SLOTS)), dtype=torch.int64, device=dev) if mode == "trace" else None
+        io = msk.make_io(w.R, w.T, [w.ctx] * w.R, h_in, h_out, ids, trace=tr, layer_out=lo)
+        say(f"[step62] gpu step, run {run} ({mode})")
         handle.verify_step(io)
+        handle.synchronize()
         torch.cuda.synchronize()
-        outs.append(h_out.cpu().numpy())
-        ids_runs.append(ids.cpu().numpy())
-        kv_runs.append([(t["k_cache"][:, :, rows].cpu().numpy().view(np.uint16),
-                         t["v_cache"][:, :, rows].cpu().numpy().view(np.uint16))
-                        for t in layers[:N_ORACLE_LAYERS]])
+        r = {"h_out": h_out.cpu().numpy(), "ids": ids.cpu().numpy()}
+        if lo is not None:
+            r["layer_out"] = lo.cpu().numpy()
+            r["kv"] = {l: (layers[l]["k_cache"][:, :, rows].cpu().numpy().view(np.uint16),
+                           layers[l]["v_cache"][:, :, rows].cpu().numpy().view(np.uint16)) for l in CHECK_LAYERS}
+        if tr is not None:
+            st = tr.cpu().numpy()
+            assert np.all(st[:, :, 0] != 0), "every workgroup of every launch stamps its start"
+        runs.append(r)
     handle.close()
 
-    # properties of the whole step
-    assert np.array_equal(outs[0], outs[1]), "repeated step differs"
-    assert np.array_equal(ids_runs[0], ids_runs[1])
-    assert np.all(np.isfinite(outs[0]))
+    a = runs[0]
+    for r, name in ((runs[1], "repeat"), (runs[2], "self-timing variant")):
+        assert np.array_equal(a["h_out"], r["h_out"]), f"{name}: h_out differs"
+        assert np.array_equal(a["ids"], r["ids"]), f"{name}: expert ids differ"
+    assert np.array_equal(a["layer_out"][L - 1], a["h_out"])
+    assert np.all(np.isfinite(a["layer_out"]))
     for l, t in enumerate(layers):
         kb, vb = before[l]
         assert np.array_equal(t["k_cache"][:, :, probe].cpu().numpy(), kb), f"layer {l}: K rows outside the verify slots changed"
         assert np.array_equal(t["v_cache"][:, :, probe].cpu().numpy(), vb), f"layer {l}: V rows outside the verify slots changed"
-    rms = float(np.sqrt(np.mean(outs[0].astype(np.float64) ** 2)))
-    say(f"[step62] h_out RMS {rms:.3f} (h_in RMS {float(np.sqrt(np.mean(h.astype(np.float64) ** 2))):.3f})")
     del layers
     torch.cuda.empty_cache()
 
-    # the oracle's own chain over the first layers
-    hh = h.astype(np.float64)
-    g_ids = ids_runs[0]
-    for l in range(N_ORACLE_LAYERS):
-        say(f"[step62] oracle layer {l} (window {w.windows[l]})")
-        lw = synth.layer_weights(w, l)
-        k, v = synth.kv_cache(w, l)
-        hh, st = orc.layer_forward(w, lw, w.R, w.T, [w.ctx], hh, k, v, w.cap, eps=w.eps)
-        m = routing_margins(st["logits"], K)
-        # Layer 0 sees the same input on both sides (logit differences come
-        # only from the fp16 attention path, ~2e-4); later layers also carry
-        # the chain's drift. A token counts when its k-th/(k+1)-th margin is
-        # well above that.
-        safe = m > (1e-3 if l == 0 else 4e-3)
-        say(f"[step62] layer {l}: min routing margin {m.min():.2e}, {int((~safe).sum())} near-tie tokens")
-        assert safe.sum() >= NT // 2, "too few tokens with a safe routing margin to check"
-        bad = routing_mismatches(g_ids[l], st["logits"], K, 1e-3 if l == 0 else 4e-3)
-        exact = int(sum(np.array_equal(g_ids[l][t], st["ids"][t]) for t in range(NT)))
-        say(f"[step62] layer {l}: {exact} of {NT} tokens with identical ranked ids")
-        for t in bad:
-            lg = st["logits"][t]
-            order = np.argsort(-lg)[:K + 2]
-            say(f"[step62] layer {l} token {t}: oracle ids {st['ids'][t].tolist()} gpu ids {g_ids[l][t].tolist()} "
-                f"top logits {[(int(e), round(float(lg[e]), 4)) for e in order]}")
-        gk, gv = kv_runs[0][l]
-        for name, got, ref in (("K", gk, k[:, :, rows]), ("V", gv, v[:, :, rows])):
+    errs = {}
+    for l in CHECK_LAYERS:
+        h_prev = h if l == 0 else a["layer_out"][l - 1]
+        errs[l] = teacher_forced_layer(w, l, h_prev, a["layer_out"][l], a["ids"][l], "step62", tol=TOL)
+        # the K/V rows the step wrote for layer l against the oracle's own
+        # projection of the same input (float tolerance plus one bf16 ulp, R19)
+        k, v = errs[l][3], errs[l][4]
+        for name, got, ref in (("K", a["kv"][l][0], k[:, :, rows]), ("V", a["kv"][l][1], v[:, :, rows])):
             g64, r64 = bf16_to_f64(got), bf16_to_f64(ref)
-            # Both sides store a float value rounded to bf16 (the cache format):
-            # values within the float tolerance may still round to neighbouring
-            # bf16 values, one bf16 ulp (2^-7 relative) apart.
             rms = float(np.sqrt(np.mean(r64 * r64)))
             bound = TOL * rms + np.ldexp(1.0, -7) * np.abs(r64)
-            worst = float(np.max(np.abs(g64 - r64) - bound))
-            say(f"[step62] layer {l}: {name} write rel err {rel_err(g64, r64):.2e}, "
-                f"{int(np.sum(g64 != r64))} of {g64.size} values differ")
-            assert worst <= 0.0, f"layer {l}: {name} write outside tolerance + one bf16 ulp"
-        assert not bad, f"layer {l}: routing differs for tokens {bad}"
-        del lw, k, v
+            assert float(np.max(np.abs(g64 - r64) - bound)) <= 0.0, f"layer {l}: {name} write"
+        errs[l] = errs[l][:3]
+    say("[step62] per-layer h_out error / RMS: " + " ".join(f"{l}:{e[0]:.2e}" for l, e in errs.items()))
