@@ -14,7 +14,12 @@ moves one value by a whole grid step, so the quantized expert sum and the
 layer output are discontinuous in the activations and no max-error bound
 holds for them (measured 1.5e-2 .. 3.4e-2 of the RMS on the layer output
 over seeds); they are gated by their RMS error, and by staying far below
-the quantization's own effect."""
+the quantization's own effect.
+
+Downstream of the quantizer (teacher forced): fed the kernel's own codes,
+block scales and gates for every selected expert, the oracle's down
+projection, gated combine and unpooler must match the kernel's expert sum and
+layer output at max|err| <= 2e-2 * RMS, the stated tolerance."""
 import numpy as np
 import pytest
 
@@ -135,6 +140,30 @@ def _check_decisions(w, g, xo_all, e, label):
     return n_blk, n_sc, n_code
 
 
+def _check_downstream(w, lw, g, label):
+    """acc and h_out from the kernel's own NVFP4 activations (every selected
+    expert's codes and scales), gates and h1, through the oracle's decode,
+    down projection (fp64 matrix product), gated combine and unpooler."""
+    ids, gates = g["ids"], g["gates"].astype(np.float64)
+    acc = np.zeros((w.NT, w.P), np.float64)
+    for e in np.unique(ids):
+        e = int(e)
+        a = orc.nvfp4_dequant(g["act_codes_all"][e], g["act_scales_all"][e], 1.0, w.NT, w.I)
+        wd = orc.nvfp4_dequant(lw["e_down"][e], lw["e_down_scale"][e], float(lw["e_tensor_scale"][e, 1]), w.P, w.I)
+        y = a @ wd.T
+        for t in range(w.NT):
+            for j in range(w.k):
+                if int(ids[t, j]) == e:
+                    acc[t] += gates[t, j] * y[t]
+    e_acc = rel_err(g["acc"], acc)
+    wup = (lw["w_unpool"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    h_ref = g["h1"].astype(np.float64) + acc @ wup.T
+    e_h = rel_err(g["h_out"], h_ref)
+    say(f"[{label}] teacher-forced on the kernel's codes: acc max|err|/RMS {e_acc:.2e}, h_out {e_h:.2e}")
+    assert e_acc <= TOL, (label, "acc", e_acc)
+    assert e_h <= TOL, (label, "h_out", e_h)
+
+
 def test_tiny_act_fp4_quantizer_and_layer():
     w = synth.WORKLOADS["tiny_swa"]
     lw, k, v, h = _inputs(w)
@@ -153,6 +182,7 @@ def test_tiny_act_fp4_quantizer_and_layer():
         if i == 0:
             assert np.array_equal(g["ids"], o["ids"]), "routing differs from the oracle on this seed"
             _check_layer(w, g, o, o_plain, "tiny-fp4")
+            _check_downstream(w, lw, g, "tiny-fp4")
     run.close()
 
 
@@ -191,3 +221,4 @@ def test_working_size_act_fp4_layer(name, layer, step):
     assert n_sc + n_code <= 0.01 * w.NT * w.I, "more flips than the activation error explains"
     assert np.array_equal(np.sort(g["ids"], axis=1), np.sort(o["ids"], axis=1)), "selection differs"
     _check_layer(w, g, o, o_plain, f"{name}-fp4")
+    _check_downstream(w, lw, g, f"{name}-fp4")
