@@ -224,6 +224,24 @@ size_t msk_workspace_bytes(const msk_config* cfg);
  * HIP device. */
 msk_status msk_create(const msk_config* cfg, void* workspace, size_t bytes, msk_handle* out);
 
+/* Bytes of the library's own static workspace (one array per GPU). */
+#define MSK_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+
+/* Like msk_create, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the handle's workspace is a static array of
+ * MSK_STATIC_WORKSPACE_BYTES that the library holds on each GPU it runs on
+ * until the process ends, instead of caller memory, and no pinned host word
+ * is taken. The call allocates no device or pinned memory (it uploads the
+ * schedule tables and clears the array's header synchronously).
+ * Returns MSK_E_CAPACITY, with a message, when msk_workspace_bytes(cfg)
+ * exceeds MSK_STATIC_WORKSPACE_BYTES. Every static handle on one GPU uses
+ * that GPU's single array: a second msk_create_static on the same GPU takes
+ * it over (the earlier handle must not be used afterwards), and calls that
+ * overlap in time on one GPU race. Device-side errors of a static handle are
+ * reported by msk_synchronize only. Release with msk_destroy. */
+msk_status msk_create_static(const msk_config* cfg, msk_handle* out);
+
 /* Register layer `layer` (0 .. n_layers-1). Pointers are borrowed. */
 msk_status msk_load_layer(msk_handle h, int32_t layer, const msk_layer_desc* desc);
 

@@ -13,6 +13,8 @@
 #include "../../include/msk.h"
 #include "msk_internal.h"
 
+static_assert(MSK_STATIC_WORKSPACE_BYTES == msk::kStaticScratchBytes, "static workspace size");
+
 namespace {
 
 using msk::kMaxGrid;
@@ -141,6 +143,8 @@ struct msk_handle_s {
   hipEvent_t done = nullptr;      // recorded after that copy (calls not under graph capture)
   bool done_pending = false;      // `done` recorded and not yet observed complete
   bool clear_err = false;         // the next call's reset zeroes the device error word
+  bool is_static = false;         // workspace = the library's static array (msk_create_static)
+  hipStream_t last_stream = nullptr;  // stream of the last call (static handles: msk_synchronize)
   uint64_t calls = 0;  // verify calls enqueued (selects the histogram buffers)
   std::string last_error;
 };
@@ -231,7 +235,11 @@ extern "C" size_t msk_workspace_bytes(const msk_config* cfg) {
   return make_layout(cfg, kMaxGrid).total;
 }
 
-extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t bytes, msk_handle* out) {
+namespace {
+
+// Shared by msk_create and msk_create_static. A static handle has no pinned
+// error word and no event: its device status is read by msk_synchronize.
+msk_status create_impl(const msk_config* cfg, void* workspace, size_t bytes, bool is_static, msk_handle* out) {
   if (!out) return fail(nullptr, MSK_E_INVALID, "out is NULL");
   *out = nullptr;
   std::string why = check_config(cfg);
@@ -269,6 +277,7 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
   if (!h) return fail(nullptr, MSK_E_INVALID, "out of host memory");
   h->cfg = *cfg;
   h->grid = G;
+  h->is_static = is_static;
   h->ws = (uint8_t*)workspace;
   h->ws_bytes = bytes;
   h->lay = lay;
@@ -331,18 +340,44 @@ extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t 
     delete h;
     return fail(nullptr, MSK_E_HIP, "hipMemcpy of the workspace header failed");
   }
-  if (hipHostMalloc((void**)&h->err_host, 256, hipHostMallocDefault) != hipSuccess) {
-    delete h;
-    return fail(nullptr, MSK_E_HIP, "hipHostMalloc of the error word failed");
-  }
-  *h->err_host = 0;
-  if (hipEventCreateWithFlags(&h->done, hipEventDisableTiming) != hipSuccess) {
-    (void)hipHostFree(h->err_host);
-    delete h;
-    return fail(nullptr, MSK_E_HIP, "hipEventCreate failed");
+  if (!is_static) {
+    if (hipHostMalloc((void**)&h->err_host, 256, hipHostMallocDefault) != hipSuccess) {
+      delete h;
+      return fail(nullptr, MSK_E_HIP, "hipHostMalloc of the error word failed");
+    }
+    *h->err_host = 0;
+    if (hipEventCreateWithFlags(&h->done, hipEventDisableTiming) != hipSuccess) {
+      (void)hipHostFree(h->err_host);
+      delete h;
+      return fail(nullptr, MSK_E_HIP, "hipEventCreate failed");
+    }
   }
   *out = h;
   return MSK_OK;
+}
+
+}  // namespace
+
+extern "C" msk_status msk_create(const msk_config* cfg, void* workspace, size_t bytes, msk_handle* out) {
+  return create_impl(cfg, workspace, bytes, false, out);
+}
+
+extern "C" msk_status msk_create_static(const msk_config* cfg, msk_handle* out) {
+  if (!out) return fail(nullptr, MSK_E_INVALID, "out is NULL");
+  *out = nullptr;
+  const size_t need = msk_workspace_bytes(cfg);
+  if (need == 0) return fail(nullptr, MSK_E_SHAPE, cfg ? check_config(cfg) : std::string("config is NULL"));
+  if (need > msk::kStaticScratchBytes) {
+    char buf[160];
+    snprintf(buf, sizeof buf, "configuration needs %zu workspace bytes; the static workspace holds %zu", need,
+             msk::kStaticScratchBytes);
+    return fail(nullptr, MSK_E_CAPACITY, buf);
+  }
+  void* ws = nullptr;
+  const hipError_t e = msk_static_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(nullptr, MSK_E_HIP, std::string("hipGetSymbolAddress of the static workspace failed: ") + hipGetErrorString(e));
+  return create_impl(cfg, ws, msk::kStaticScratchBytes, true, out);
 }
 
 extern "C" msk_status msk_load_layer(msk_handle h, int32_t layer, const msk_layer_desc* d) {
@@ -386,12 +421,25 @@ msk::LayerW to_w(const msk_layer_desc& d) {
   return w;
 }
 
+msk_status report_device_error(msk_handle h, int32_t e);
+
 // Device status of completed calls: the error word a call copied back once
 // its event shows the copy landed (or when no eager call is pending, a copy
 // made by a graph replay). A nonzero word is reported once; the device word
 // stays set (every later launch does nothing) until the next call's reset
 // clears it.
 msk_status poll_device_status(msk_handle h, bool wait) {
+  if (h->is_static) {
+    // no pinned copy: only msk_synchronize reads the word, synchronously
+    if (!wait) return MSK_OK;
+    if (hipStreamSynchronize(h->last_stream) != hipSuccess) return fail(h, MSK_E_HIP, "hipStreamSynchronize failed");
+    int32_t word = 0;
+    if (hipMemcpy(&word, h->ws + h->lay.err, sizeof word, hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(h, MSK_E_HIP, "reading the device error word failed");
+    if (word == 0) return MSK_OK;
+    h->clear_err = true;
+    return report_device_error(h, word);
+  }
   if (h->done_pending) {
     hipError_t q = wait ? hipEventSynchronize(h->done) : hipEventQuery(h->done);
     if (q == hipErrorNotReady) return MSK_OK;
@@ -402,6 +450,10 @@ msk_status poll_device_status(msk_handle h, bool wait) {
   if (e == 0) return MSK_OK;
   __atomic_store_n(h->err_host, 0, __ATOMIC_RELEASE);
   h->clear_err = true;
+  return report_device_error(h, e);
+}
+
+msk_status report_device_error(msk_handle h, int32_t e) {
   if (e == MSK_E_INVALID)
     return fail(h, MSK_E_INVALID, "a previous call was given an invalid ctx_len or tree_mask (its outputs are invalid)");
   if (e == MSK_E_CAPACITY)
@@ -497,6 +549,8 @@ int barriers_of(uint32_t mode) {
 
 msk_status finish(msk_handle h, hipStream_t s) {
   const Layout& L = h->lay;
+  h->last_stream = s;
+  if (h->is_static) return MSK_OK;  // status read by msk_synchronize
   if (hipMemcpyAsync(h->err_host, h->ws + L.err, 4, hipMemcpyDeviceToHost, s) != hipSuccess)
     return fail(h, MSK_E_HIP, "hipMemcpyAsync of the error word failed");
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;

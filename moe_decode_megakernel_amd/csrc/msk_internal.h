@@ -25,6 +25,7 @@ constexpr int kMaxQSlices = 2;             // split-K slices of the Q projection
 constexpr int kMaxSplits = 64;             // attention splits per (request, kv head)
 constexpr int kMaxPrefetch = 32;           // experts in a speculative prefetch list
 constexpr int kMaxRouterPerWg = 2;         // router (expert, k-slice) pairs per workgroup
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;  // the library's own workspace array per device
 
 // k-slices of 128 elements per row of the down projection: its block scales
 // are stored tiled, [E][P/16][dn_scale_slices(I)][16 rows][8], so one wave's
@@ -148,6 +149,9 @@ struct Params {
 hipError_t msk_launch_layer(const msk::Params& p, int grid, bool debug, hipStream_t s);
 hipError_t msk_launch_pack_down_scale(const uint8_t* src, uint8_t* dst, int E, int P, int I, hipStream_t s);
 hipError_t msk_launch_reset(uint32_t* bar, int32_t* err, bool clear_err, hipStream_t s);
+// Device address of the library's static workspace array on the current
+// device (looked up once per device and kept).
+hipError_t msk_static_scratch(void** out);
 // Fewest layer-kernel workgroups of kThreads that one compute unit can hold,
 // over the kernel's instantiations (the grid must be co-resident).
 int msk_layer_min_occupancy();

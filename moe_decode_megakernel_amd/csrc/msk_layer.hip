@@ -22,6 +22,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "msk_internal.h"
 
@@ -2442,4 +2443,35 @@ int msk_layer_min_occupancy() {
   int m = v[0];
   for (int x : v) m = std::min(m, x);
   return m;
+}
+
+// Workspace of handles made by msk_create_static, for callers that cannot
+// allocate device memory: one array per GPU the library runs on, held until
+// the process ends. Host code never uses the array's name as an address (on
+// the host it only stands for the symbol): its device address is looked up
+// once per device with hipGetSymbolAddress, with that device current, and
+// that address is what the handles, the kernels and the copies use.
+static __device__ __align__(256) uint8_t scratch[msk::kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t msk_static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
 }

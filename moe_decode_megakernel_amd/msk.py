@@ -17,7 +17,7 @@ STATUS_NAMES = ["MSK_OK", "MSK_E_INVALID", "MSK_E_SHAPE", "MSK_E_ALIGN", "MSK_E_
 MSK_FLAG_NO_NORM = 0x1
 MSK_FLAG_ACT_FP4 = 0x2
 
-EXPORTS = ("msk_workspace_bytes", "msk_create", "msk_load_layer", "msk_verify_layer",
+EXPORTS = ("msk_workspace_bytes", "msk_create", "msk_create_static", "msk_load_layer", "msk_verify_layer",
            "msk_verify_step", "msk_synchronize", "msk_destroy", "msk_down_scale_bytes",
            "msk_pack_down_scale", "msk_last_error")
 
@@ -75,6 +75,8 @@ def lib():
         L.msk_workspace_bytes.restype = ctypes.c_size_t
         L.msk_create.argtypes = [ctypes.POINTER(msk_config), vp, ctypes.c_size_t, ctypes.POINTER(vp)]
         L.msk_create.restype = i32
+        L.msk_create_static.argtypes = [ctypes.POINTER(msk_config), ctypes.POINTER(vp)]
+        L.msk_create_static.restype = i32
         L.msk_load_layer.argtypes = [vp, i32, ctypes.POINTER(msk_layer_desc)]
         L.msk_load_layer.restype = i32
         L.msk_verify_layer.argtypes = [vp, i32, ctypes.POINTER(msk_io), vp]
@@ -112,6 +114,17 @@ def msk_create(cfg: msk_config, workspace_ptr: int, nbytes: int):
     if st != MSK_OK:
         raise MskError(st, msk_last_error(None))
     return h
+
+
+def msk_create_static(cfg: msk_config):
+    h = vp()
+    st = lib().msk_create_static(ctypes.byref(cfg), ctypes.byref(h))
+    if st != MSK_OK:
+        raise MskError(st, msk_last_error(None))
+    return h
+
+
+MSK_STATIC_WORKSPACE_BYTES = 32 << 20
 
 
 def msk_load_layer(h, layer: int, desc: msk_layer_desc) -> int:
@@ -209,9 +222,16 @@ def make_debug(t: Dict, dq_expert: int = -1) -> msk_debug:
 class Handle:
     """Owns a workspace tensor and a library handle (convenience wrapper)."""
 
-    def __init__(self, cfg: msk_config, device="cuda"):
+    def __init__(self, cfg: msk_config, device="cuda", static=False):
+        """static: use the library's own static workspace (msk_create_static)
+        instead of a workspace tensor."""
         import torch
         self.cfg = cfg
+        self.layers = {}
+        self.workspace = None
+        if static:
+            self.h = msk_create_static(cfg)
+            return
         n = msk_workspace_bytes(cfg)
         if n == 0:
             raise MskError(MSK_E_SHAPE, "configuration rejected by msk_workspace_bytes")
@@ -219,7 +239,6 @@ class Handle:
         base = self.workspace.data_ptr()
         self.ws_ptr = (base + 255) // 256 * 256
         self.h = msk_create(cfg, self.ws_ptr, n)
-        self.layers = {}
 
     def check(self, st):
         if st != MSK_OK:
