@@ -85,6 +85,13 @@ typedef enum {
  * saturating at 448), codes E2M1(x / s) (nearest even, saturating at 6, sign
  * kept; 0 when s = 0), and the down projection reads E2M1(code) * s. */
 #define MSK_FLAG_ACT_FP4 0x2u
+/* Tail prefetch of the next layer's KV window (orcarouter.ai, "Su cosa
+ * vengono ancora spesi i 5,9 ms": old KV rows are loaded ahead while the
+ * previous operations finish). During the next layer's QKV projection at the
+ * end of each launch, the workgroups read one word of every 128-byte line of
+ * the prior K and V rows that layer's attention will read, so that the next
+ * launch finds them in the memory-side cache. No effect on results. */
+#define MSK_FLAG_KV_PREFETCH 0x4u
 
 typedef struct {
   int32_t hidden;        /* H, multiple of 128; nq*d also a multiple of 128 */

@@ -180,7 +180,7 @@ std::string check_config(const msk_config* c) {
   if (c->max_requests <= 0 || c->max_requests > msk::kMaxReq) return "max_requests must be in 1..4";
   if (c->kv_capacity <= 0) return "kv_capacity must be positive";
   if (!(c->rms_eps >= 0.0f)) return "rms_eps must be >= 0";
-  if ((c->flags & ~(MSK_FLAG_NO_NORM | MSK_FLAG_ACT_FP4)) != 0) return "unknown flag bits";
+  if ((c->flags & ~(MSK_FLAG_NO_NORM | MSK_FLAG_ACT_FP4 | MSK_FLAG_KV_PREFETCH)) != 0) return "unknown flag bits";
   if (c->expert_prefetch < 0 || c->expert_prefetch > msk::kMaxPrefetch || c->expert_prefetch > c->n_experts)
     return "expert_prefetch must be in 0..min(32, n_experts)";
   return std::string();
@@ -525,6 +525,11 @@ msk::Params base_params(msk_handle h, const msk_io* io) {
   p.logits = reinterpret_cast<float*>(ws + L.logits);
   p.ppart = reinterpret_cast<float*>(ws + L.ppart);
   p.abuf = reinterpret_cast<uint16_t*>(ws + L.abuf);
+  {
+    const size_t nsel = std::min<size_t>((size_t)c.n_experts, (size_t)pass_tokens(&c) * c.top_k);
+    p.acode = ws + L.abuf;
+    p.ascale = ws + L.abuf + nsel * pass_tokens(&c) * c.expert_inter / 2;
+  }
   p.accpart = reinterpret_cast<float*>(ws + L.accpart);
   {
     int32_t* hist = reinterpret_cast<int32_t*>(ws + L.hist);
@@ -537,6 +542,7 @@ msk::Params base_params(msk_handle h, const msk_io* io) {
   p.wg_units = h->wg_units;
   p.wg_nunits = h->wg_nunits;
   p.n_prefetch = c.expert_prefetch;
+  p.kv_prefetch = (c.flags & MSK_FLAG_KV_PREFETCH) ? 1 : 0;
   return p;
 }
 

@@ -125,7 +125,9 @@ struct Params {
   uint16_t* attn;         // fp16 [NT][Dq] merged attention output
   float* logits;          // [p_slices][NT][E] router subtree sums per k-slice (no bias)
   float* ppart;           // [p_slices][NT][P]
-  uint16_t* abuf;         // f16 [n_sel_max][NT][I]
+  uint16_t* abuf;         // f16 [n_sel_max][NT][I] (SwiGLU output x gate weight)
+  uint8_t* acode;         // with act_fp4, in abuf's region: E2M1 codes [n_sel_max][NT][I/2]
+  uint8_t* ascale;        //   and E4M3 block scales [n_sel_max][NT][I/16]
   float* accpart;         // [parts][NT][P]
   const int32_t* hist_rd; // [n_layers][E] selection counts of the previous call (prefetch ranking)
   int32_t* hist_wr;       // [n_layers][E] this call's counts
@@ -134,6 +136,7 @@ struct Params {
   const Unit* wg_units;     // QKV (own and next layer share shapes), O proj, pool, unpool
   const int32_t* wg_nunits;
   int32_t n_prefetch;     // experts to prefetch speculatively (0 = off)
+  int32_t kv_prefetch;    // touch the next layer's KV window during its QKV projection
   // outputs
   int32_t* out_ids;       // [NT][k] or NULL
   float* out_gates;

@@ -1403,7 +1403,8 @@ __device__ __forceinline__ float route_logit(const RouteLoads& L, int S, int tt,
 // loads are in flight while the top-k runs: X = fp16 of the sum over the
 // n <= kMaxPSlices slices of fp32 [n][NT][K], in slice order from +0 (the
 // arithmetic of fill_x_sum), items as in fill_x_sum, kSumBatch items per
-// thread per batch (one batch covers K <= 2048). Loads are unconditional
+// thread per batch (two batches cover K <= 2048; the first is in flight during
+// the top-k). Loads are unconditional
 // (slice and token indices clamped in range).
 constexpr int kSumBatch = 4;
 static_assert(2 * kSumBatch * kThreads >= kMaxTok * 2048 / 8, "two batches cover the pooled tile");
@@ -1867,8 +1868,10 @@ __device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
   __syncthreads();
   const int NT = p.NT;
   if (p.act_fp4) {
-    // quantize: one (unit pair, token) block of 16 per item, 32 B to
-    // abuf[j][token][it*8 .. +16] as fp16(value * gate weight)
+    // quantize: one (unit pair, token) block of 16 per item: 8 B of E2M1
+    // codes to acode[j][token][it*4 ..] and the E4M3 block scale to
+    // ascale[j][token][it/2] (the gate weight is applied after the down
+    // projection)
     for (int q = threadIdx.x; q < (u1 - u0) / 2 * NT; q += kThreads) {
       const int pl = q / NT, tok = q - pl * NT;
       const int u = u0 + 2 * pl, j = u / ntile, it = u - j * ntile;
@@ -1885,18 +1888,16 @@ __device__ __forceinline__ void gemm1_phase(const Params& p, Smem& sm) {
       for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
       const uint32_t sc = e4m3_code_rne_sat(amax / 6.0f);
       const float s = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
-      const float gw = rt.tokgate[j][tok];
-      uint32_t codes[2] = {0u, 0u}, hv[8];
+      uint32_t codes[2] = {0u, 0u};
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const uint32_t c = e2m1_code_rne_sat(s > 0.0f ? x[i] / s : 0.0f);
         codes[i >> 3] |= c << ((i & 7) * 4);
-        const uint16_t h = f2h(e2m1_value(c) * s * gw);
-        hv[i >> 1] = (i & 1) ? (hv[i >> 1] | ((uint32_t)h << 16)) : (uint32_t)h;
       }
-      uint16_t* dst = p.abuf + ((size_t)j * NT + tok) * I + it * 8;
-      st_wt16(dst, u32x4_t{hv[0], hv[1], hv[2], hv[3]});
-      st_wt16(dst + 8, u32x4_t{hv[4], hv[5], hv[6], hv[7]});
+      const size_t row = (size_t)j * NT + tok;
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(p.acode + row * (I / 2) + it * 4),
+                         (uint64_t)codes[0] | ((uint64_t)codes[1] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ascale + row * (I / 16) + it / 2, (uint8_t)sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if constexpr (debug) {
         if (p.dbg.act_codes_all) {
           const size_t row = (size_t)rt.sel[j] * NT + tok;
@@ -1964,6 +1965,88 @@ __device__ __forceinline__ void g2_issue(const Params& p, const Route& rt, int j
   }
 }
 
+// GEMM2 with NVFP4 activations: the A operand is read as E2M1 codes (16 B)
+// and two E4M3 block scales per lane and expert, a quarter of the fp16
+// bytes, and decoded like the weights (exact in fp16); the ring holds
+// kG2Ring4 experts. The gate weight of each token multiplies the fp32 MFMA
+// output together with the tensor scale.
+constexpr int kG2Ring4 = 6;
+
+struct G2Slot4 {
+  uint4 c;
+  uint32_t s;
+  uint4 ac;
+  uint32_t as;
+};
+
+__device__ __forceinline__ void g2_issue4(const Params& p, const Route& rt, int j, int tile, G2Slot4& b) {
+  const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4, w = wave_id();
+  const int I = p.I, P = p.P;
+  const int e = rt.sel[j];
+  const int k = w * 128 + g_ * 32;
+  const bool kv = k < I;
+  const int kk = kv ? k : 0;
+  const int row = tile * 16 + r_;
+  b.c = *reinterpret_cast<const uint4*>(p.cur.e_dn + (size_t)e * P * (I / 2) + (size_t)row * (I / 2) + kk / 2);
+  const int nsl = dn_scale_slices(I);
+  b.s = *reinterpret_cast<const uint16_t*>(p.cur.e_dn_sc + (((size_t)e * (P / 16) + tile) * nsl + min(w, nsl - 1)) * 128 +
+                                           r_ * 8 + g_ * 2);
+  const bool routed = kv && r_ < p.NT && rt.tokgate[j][r_] != 0.0f;
+  if (routed) {
+    const size_t arow = (size_t)j * p.NT + r_;
+    b.ac = *reinterpret_cast<const uint4*>(p.acode + arow * (I / 2) + k / 2);
+    b.as = *reinterpret_cast<const uint16_t*>(p.ascale + arow * (I / 16) + k / 16);
+  } else {
+    b.ac = make_uint4(0, 0, 0, 0);
+    b.as = 0u;
+  }
+}
+
+template <bool debug>
+__device__ __forceinline__ f32x4_t gemm2_fp4_loop(const Params& p, const Route& rt, int tile, int j0, int j1) {
+  const int lane = lane_id(), r_ = lane & 15, g_ = lane >> 4, w = wave_id();
+  const int I = p.I;
+  f32x4_t total = {0.f, 0.f, 0.f, 0.f};
+  G2Slot4 ring[kG2Ring4];
+#pragma unroll
+  for (int i = 0; i < kG2Ring4; ++i) {
+    g2_issue4(p, rt, min(j0 + i, j1 - 1), tile, ring[i]);
+    ring_fence();
+  }
+  for (int base = j0; base < j1; base += kG2Ring4) {
+#pragma unroll
+    for (int i = 0; i < kG2Ring4; ++i) {
+      const int jj = base + i;
+      const int jc = min(jj, j1 - 1);
+      uint4 av[4], bw[4];
+      fp4_decode(ring[i].ac, ring[i].as, av);
+      fp4_decode(ring[i].c, ring[i].s, bw);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = mfma_f16(av[q], bw[q], acc);
+      // acc[c] is token 4g+c of row r: its gate weight times the tensor scale
+      const float ts = jj < j1 ? rt.ts_dn[jc] : 0.0f;
+      const float4 gt = *reinterpret_cast<const float4*>(&rt.tokgate[jc][4 * g_]);
+      total[0] = fmaf(acc[0], ts * gt.x, total[0]);
+      total[1] = fmaf(acc[1], ts * gt.y, total[1]);
+      total[2] = fmaf(acc[2], ts * gt.z, total[2]);
+      total[3] = fmaf(acc[3], ts * gt.w, total[3]);
+      if constexpr (debug) {
+        const int e = rt.sel[jc];
+        const int k = w * 128 + g_ * 32;
+        if (jj < j1 && k < I && p.dbg.dq_dn && e == p.dbg.dq_expert) {
+          uint4* dst = reinterpret_cast<uint4*>(p.dbg.dq_dn + (size_t)(tile * 16 + r_) * I + k);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dst[q] = bw[q];
+        }
+      }
+      g2_issue4(p, rt, min(jj + kG2Ring4, j1 - 1), tile, ring[i]);
+      ring_fence();
+    }
+  }
+  return total;
+}
+
 template <bool debug>
 __device__ __forceinline__ void gemm2_phase(const Params& p, Smem& sm) {
   Route& rt = route_of(sm);
@@ -1975,7 +2058,9 @@ __device__ __forceinline__ void gemm2_phase(const Params& p, Smem& sm) {
   const int tile = blockIdx.x % tiles, part = blockIdx.x / tiles;
   const int j0 = part * rt.n_sel / parts, j1 = (part + 1) * rt.n_sel / parts;
   f32x4_t total = {0.f, 0.f, 0.f, 0.f};
-  if (j0 < j1) {
+  if (j0 < j1 && p.act_fp4) {
+    total = gemm2_fp4_loop<debug>(p, rt, tile, j0, j1);
+  } else if (j0 < j1) {
     G2Slot ring[kG2Ring];
 #pragma unroll
     for (int i = 0; i < kG2Ring; ++i) {
@@ -2101,6 +2186,37 @@ __device__ __forceinline__ void prefetch_experts(const Params& p, const Smem& sm
       v[q] = *reinterpret_cast<const uint32_t*>(base[reg] + (size_t)sm.plist[j] * bytes[reg] + off);
     }
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  // never true (layer >= 0); keeps the loads
+  if (p.layer < 0 && acc == 0x9E3779B9u) p.err[1] = (int32_t)acc;
+}
+
+// Reads one dword of every 128-byte line of the prior K and V rows that the
+// next layer's attention will read (the window of every request and kv
+// head; the verify tokens' own rows are being written in this phase and are
+// left alone), so that the next launch finds them in the memory-side cache.
+// This workgroup takes lines blockIdx.x, blockIdx.x + G, ... of the list.
+__device__ __forceinline__ void prefetch_next_kv(const Params& p, const Smem& sm) {
+  const LayerW& lw = p.nxt;
+  const int lines_per_row = p.d * 2 / 128;  // 1 (d = 64) or 2 (d = 128)
+  uint32_t acc = 0;
+  int done = 0;  // lines of earlier (request, kv head) ranges
+  for (int r = 0; r < p.R; ++r) {
+    const int ctx = ctx_uni(sm, r);
+    const int lo = lw.window > 0 ? max(0, ctx - lw.window + 1) : 0;
+    const int nrows = max(0, ctx - lo);  // prior rows only
+    const int nl = nrows * lines_per_row;
+    for (int g = 0; g < p.nkv; ++g) {
+      const size_t row0 = ((size_t)r * p.nkv + g) * p.cap + lo;
+      for (int l = (int)(blockIdx.x * kThreads + threadIdx.x) - done; l < 2 * nl; l += gridDim.x * kThreads) {
+        if (l < 0) continue;
+        const uint16_t* base = l < nl ? lw.k_cache : lw.v_cache;
+        const int ll = l < nl ? l : l - nl;
+        acc ^= *reinterpret_cast<const uint32_t*>(base + (row0 + ll / lines_per_row) * p.d + (ll % lines_per_row) * 64);
+      }
+      done += 2 * nl;
+      done %= gridDim.x * kThreads;
+    }
   }
   // never true (layer >= 0); keeps the loads
   if (p.layer < 0 && acc == 0x9E3779B9u) p.err[1] = (int32_t)acc;
@@ -2349,6 +2465,7 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
     mark(kTrUnpoolBar);
     fill_x_qkv(p, p.h_out, p.ssq2, p.nxt.g_attn, sm);
     mark(kTrQkvFill);
+    if (p.kv_prefetch) prefetch_next_kv(p, sm);
     EpiArgs ea{p.nxt.k_cache, p.nxt.v_cache, nullptr, p.qpart, nullptr, nullptr, nullptr};
     dense_phase<Epi::Qkv>(p, kSchQkv, p.nxt.w_qkv, p.H, p.H, ea, sm, ring);
     mark(kTrQkvNext);

@@ -16,6 +16,7 @@ STATUS_NAMES = ["MSK_OK", "MSK_E_INVALID", "MSK_E_SHAPE", "MSK_E_ALIGN", "MSK_E_
                 "MSK_E_CAPACITY", "MSK_E_HIP", "MSK_E_TIMEOUT"]
 MSK_FLAG_NO_NORM = 0x1
 MSK_FLAG_ACT_FP4 = 0x2
+MSK_FLAG_KV_PREFETCH = 0x4
 
 EXPORTS = ("msk_workspace_bytes", "msk_create", "msk_create_static", "msk_load_layer", "msk_verify_layer",
            "msk_verify_step", "msk_synchronize", "msk_destroy", "msk_down_scale_bytes",

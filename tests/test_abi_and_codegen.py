@@ -57,10 +57,11 @@ def test_error_paths_without_a_device():
     assert msk.msk_workspace_bytes(bad) == 0
     bad = msk.make_config(w, max_tokens=32)
     assert msk.msk_workspace_bytes(bad) == 0
-    # flags: the NVFP4-activation flag is accepted, unknown bits are not
+    # flags: the NVFP4-activation and KV-prefetch flags are accepted, unknown bits are not
     assert msk.msk_workspace_bytes(msk.make_config(w, flags=msk.MSK_FLAG_ACT_FP4)) > 0
     assert msk.msk_workspace_bytes(msk.make_config(w, flags=msk.MSK_FLAG_NO_NORM | msk.MSK_FLAG_ACT_FP4)) > 0
-    assert msk.msk_workspace_bytes(msk.make_config(w, flags=0x4)) == 0
+    assert msk.msk_workspace_bytes(msk.make_config(w, flags=msk.MSK_FLAG_KV_PREFETCH)) > 0
+    assert msk.msk_workspace_bytes(msk.make_config(w, flags=0x8)) == 0
     assert msk.lib().msk_destroy(None) == msk.MSK_E_INVALID
 
 

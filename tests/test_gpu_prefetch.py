@@ -83,3 +83,36 @@ def test_prefetch_list_working_size_layer():
     handle.close()
     del t
     torch.cuda.empty_cache()
+
+
+def test_kv_tail_prefetch_changes_no_output():
+    """MSK_FLAG_KV_PREFETCH only reads the next layer's KV window: a step with
+    the flag gives the same bytes as one without (several requests with
+    different contexts, so every request's window is walked)."""
+    import torch
+    from dataclasses import replace
+    dev = "cuda"
+    w = replace(synth.small_stack(3), R=4, T=4)
+    h = synth.h_input(w)
+    outs = []
+    for flags in (0, msk.MSK_FLAG_KV_PREFETCH):
+        handle = msk.Handle(msk.make_config(w, flags=flags))
+        keep = []
+        for l in range(w.n_layers):
+            lw = synth.layer_weights(w, l)
+            k, v = synth.kv_cache(w, l)
+            t = synth.to_device(lw, dev)
+            t["k_cache"] = torch.from_numpy(k.view(np.int16)).to(dev)
+            t["v_cache"] = torch.from_numpy(v.view(np.int16)).to(dev)
+            handle.load_layer(l, t, int(lw["window"]))
+            keep.append(t)
+        h_in = torch.from_numpy(np.ascontiguousarray(h, np.float32)).to(dev)
+        h_out = torch.zeros_like(h_in)
+        ids = torch.zeros((w.n_layers, w.NT, w.k), dtype=torch.int32, device=dev)
+        handle.verify_step(msk.make_io(w.R, w.T, [64, 50, 20, 3], h_in, h_out, ids))
+        handle.synchronize()
+        outs.append((h_out.cpu().numpy(), ids.cpu().numpy(), [t["k_cache"].cpu().numpy() for t in keep]))
+        handle.close()
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    for a, b in zip(outs[0][2], outs[1][2]):
+        assert np.array_equal(a, b)
