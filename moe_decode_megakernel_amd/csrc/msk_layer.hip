@@ -882,6 +882,10 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
   constexpr int VS = kAttnChunk + 4;      // V^T tile row stride (elements): Vt[d][key]
   uint16_t* Ks = reinterpret_cast<uint16_t*>(sm.x);
   uint16_t* Vt = Ks + kAttnChunk * RS;
+  uint16_t* Ks1 = Vt + D * VS;  // second buffer
+  uint16_t* Vt1 = Ks1 + kAttnChunk * RS;
+  static_assert((2 * kAttnChunk * (kMaxHeadDim + 8) + 2 * kMaxHeadDim * (kAttnChunk + 4)) * 2 <= kXBytes,
+                "two K/V chunk buffers fit the X region");
 
   const float scale_log2 = rsqrtf((float)D) * 1.4426950408889634f;
   float m_run = -INFINITY, l_run = 0.0f;
@@ -916,7 +920,7 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
       vr[j] = *reinterpret_cast<const uint4*>(vc + (size_t)min(kb + vkey, it.k_end - 1) * D + vc8);
     }
   };
-  auto stage_chunk = [&](const uint4 (&kr)[PER], const uint4 (&vr)[PER]) {
+  auto stage_chunk = [&](const uint4 (&kr)[PER], const uint4 (&vr)[PER], uint16_t* Ks, uint16_t* Vt) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       int i = threadIdx.x + j * kThreads;
@@ -976,28 +980,12 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
   }
 
   trace_stamp(trace_row, kTrAttnQ);
-  for (int c0 = 0; c0 < nchunks; c0 += 2) {
-#pragma unroll
-   for (int half = 0; half < 2; ++half) {
-    const int c = c0 + half;
-    __syncthreads();
-    if (half == 0) {
-      stage_chunk(kreg0, vreg0);
-      load_chunk(c + 2, kreg0, vreg0);
-    } else {
-      stage_chunk(kreg1, vreg1);
-      load_chunk(c + 2, kreg1, vreg1);
-    }
-    ring_fence();
-    __syncthreads();
-    if (c == 0) trace_stamp(trace_row, kTrAttnKv);
-    if (!active || c >= nchunks) continue;
+  // One 64-key chunk: scores for 4 key tiles of 16 (the K reads and MFMAs of
+  // all four tiles first, independent accumulators each summed over s in
+  // order), then the mask, evaluated without short-circuit branches, the
+  // online softmax in base 2, and O^T += V^T P^T over two 32-key steps.
+  auto compute_chunk = [&](int c, const uint16_t* Kb, const uint16_t* Vb) {
     const int kb = it.k_begin + c * kAttnChunk;
-    // scores for 4 key tiles of 16: the K reads and MFMAs of all four tiles
-    // first (independent accumulators, each summed over s in order), then the
-    // mask, evaluated without short-circuit branches. A mask between the
-    // tiles splits the code into blocks the scheduler cannot overlap, and the
-    // tiles then pay their LDS and MFMA latencies one after the other.
     f32x4_t s4v[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) s4v[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1005,7 +993,7 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const uint4 a = *reinterpret_cast<const uint4*>(Ks + (kt * 16 + r_) * RS + s * 32 + g_ * 8);
+        const uint4 a = *reinterpret_cast<const uint4*>(Kb + (kt * 16 + r_) * RS + s * 32 + g_ * 8);
         s4v[kt] = mfma_f16(a, qb[s], s4v[kt]);
       }
     float sc[4][4];
@@ -1049,7 +1037,6 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
     m_run = m_new;
 #pragma unroll
     for (int i = 0; i < DT; ++i) o[i] *= alpha;
-    // O^T += V^T P^T over two 32-key steps
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       uint4 bp;
@@ -1060,14 +1047,36 @@ __device__ __forceinline__ void attention_phase(const Params& p, const LayerW& l
       const int k0 = u * 32 + 4 * g_;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vrow = Vt + (dt * 16 + r_) * VS;
+        const uint16_t* vrow = Vb + (dt * 16 + r_) * VS;
         const uint2 lo = *reinterpret_cast<const uint2*>(vrow + k0);
         const uint2 hi = *reinterpret_cast<const uint2*>(vrow + k0 + 16);
         uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
         o[dt] = mfma_f16(av, bp, o[dt]);
       }
     }
-   }
+  };
+  // Two LDS buffers: chunk c+1 is staged (from registers) while chunk c is
+  // computed from the other buffer, with one workgroup barrier per chunk.
+  // Register sets A (even chunks) and B (odd chunks) hold the next two
+  // chunks' loads; every load is issued (past the item's end it re-reads the
+  // item's last row), so the wait counts stay static.
+  stage_chunk(kreg0, vreg0, Ks, Vt);
+  load_chunk(2, kreg0, vreg0);
+  ring_fence();
+  __syncthreads();
+  trace_stamp(trace_row, kTrAttnKv);
+  for (int c0 = 0; c0 < nchunks; c0 += 2) {
+    if (c0 + 1 < nchunks) stage_chunk(kreg1, vreg1, Ks1, Vt1);
+    load_chunk(c0 + 3, kreg1, vreg1);
+    ring_fence();
+    if (active) compute_chunk(c0, Ks, Vt);
+    __syncthreads();
+    if (c0 + 1 >= nchunks) break;
+    if (c0 + 2 < nchunks) stage_chunk(kreg0, vreg0, Ks, Vt);
+    load_chunk(c0 + 4, kreg0, vreg0);
+    ring_fence();
+    if (active) compute_chunk(c0 + 1, Ks1, Vt1);
+    __syncthreads();
   }
   if (active && r_ < p.T) {
     float* rec = apart_at(p, blockIdx.x, w, r_);
