@@ -2231,61 +2231,60 @@ __device__ __forceinline__ void prefetch_next_kv(const Params& p, const Smem& sm
   if (p.layer < 0 && acc == 0x9E3779B9u) p.err[1] = (int32_t)acc;
 }
 
-// Copies this workgroup's units of every dense schedule to LDS (one round
-// trip; readers wait on a later workgroup barrier).
-__device__ __forceinline__ void stage_units(const Params& p, Smem& sm) {
-  constexpr int kN = kSchCount * kMaxWgUnits;
-  static_assert(kN + kSchCount <= kThreads, "one entry per thread");
-  if (threadIdx.x < kN) {
-    (&sm.units[0][0])[threadIdx.x] = p.wg_units[(size_t)blockIdx.x * kN + threadIdx.x];
-  } else if (threadIdx.x < kN + kSchCount) {
-    const int i = threadIdx.x - kN;
-    sm.nunits[i] = p.wg_nunits[(size_t)blockIdx.x * kSchCount + i];
-  }
-}
-
 // Device error codes (the numbers of the matching msk_status values).
 constexpr int32_t kErrInvalid = 1;   // a token mask breaks the tree rules, or ctx_len < 0
 constexpr int32_t kErrCapacity = 5;  // ctx_len + n_tokens > kv_capacity
 
-// Request metadata of the launch, from device memory (one round trip,
-// together with the error word and this workgroup's schedule rows): the
-// pass's context lengths and token masks go to LDS, wave 0 checks them and
-// packs the token depths. Every workgroup reads the same words and takes the
-// same decision, so either all of them run the launch or none does. Returns
-// false when the launch must do nothing: an earlier launch failed (the error
-// word is sticky until the host has read it) or the metadata is invalid
-// (workgroup 0 then records the error code).
+// Launch prologue: this workgroup's units of every dense schedule, the pass's
+// context lengths and token masks, and the device error word, all read from
+// device memory in one round trip (every load is unconditional with a
+// clamped index, and the LDS writes follow the last load), then wave 0 checks
+// the metadata and packs the token depths. Every workgroup reads the same
+// words and takes the same decision, so either all of them run the launch or
+// none does. Returns false when the launch must do nothing: an earlier launch
+// failed (the error word is sticky until the host has read it) or the
+// metadata is invalid (workgroup 0 then records the error code).
 //   ctx: 0 <= ctx, ctx + T <= cap.
 //   masks: bit t set, no bit above t, and each ancestor's mask contained in
 //   the token's own (the tree rules of the causal verify pass).
-__device__ __forceinline__ bool load_request_meta(const Params& p, Smem& sm) {
+__device__ __forceinline__ bool load_launch_words(const Params& p, Smem& sm) {
+  constexpr int kN = kSchCount * kMaxWgUnits;
+  static_assert(kN + kSchCount <= kThreads && kMaxReq * kMaxTok <= kThreads, "one entry per thread");
   const int tid = threadIdx.x;
-  if (tid < p.R) sm.ctx[tid] = p.ctx_dev[p.r0 + tid];
+  const int mr = tid / kMaxTok, mt = tid % kMaxTok;  // (request, token) of this thread's mask
+  static_assert(sizeof(Unit) == sizeof(uint4), "a unit is one 16-byte load");
+  const uint4 u = *reinterpret_cast<const uint4*>(p.wg_units + (size_t)blockIdx.x * kN + min(tid, kN - 1));
+  const int32_t nu = p.wg_nunits[(size_t)blockIdx.x * kSchCount + min(max(tid - kN, 0), kSchCount - 1)];
+  const int32_t c = p.ctx_dev[p.r0 + min(tid, p.R - 1)];
+  const uint16_t* tsrc = p.tree_dev ? p.tree_dev + (size_t)(p.r0 + min(mr, p.R - 1)) * p.T + min(mt, p.T - 1) : p.zeros;
+  const uint16_t tm = *tsrc;
+  const int32_t e0 = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  ring_fence();
+  if (tid < kN) reinterpret_cast<uint4*>(&sm.units[0][0])[tid] = u;
+  else if (tid < kN + kSchCount) sm.nunits[tid - kN] = nu;
+  if (tid < p.R) sm.ctx[tid] = c;
   if (tid < kMaxReq * kMaxTok) {
-    const int r = tid / kMaxTok, t = tid % kMaxTok;
     uint32_t a = 0;
-    if (r < p.R && t < p.T) a = p.tree_dev ? (uint32_t)p.tree_dev[(size_t)(p.r0 + r) * p.T + t] : ((2u << t) - 1u);
-    sm.tanc[r][t] = a;
+    if (mr < p.R && mt < p.T) a = p.tree_dev ? (uint32_t)tm : ((2u << mt) - 1u);
+    sm.tanc[mr][mt] = a;
   }
-  if (tid == 0) sm.err0 = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) sm.err0 = e0;
   __syncthreads();
   if (wave_id() == 0) {
     const int lane = lane_id(), r = lane / kMaxTok, t = lane % kMaxTok;
     const bool live = r < p.R && t < p.T;
     const uint32_t a = sm.tanc[r][t];
-    bool ok = true;
-    if (live) {
-      ok = ((a >> t) & 1u) != 0u && (a >> (t + 1)) == 0u;
-      for (int u = 0; u < kMaxTok; ++u)
-        if (u < t && ((a >> u) & 1u) != 0u && (sm.tanc[r][u] & ~a) != 0u) ok = false;
-    }
+    uint32_t anc[kMaxTok];
+#pragma unroll
+    for (int v = 0; v < kMaxTok; ++v) anc[v] = sm.tanc[r][v];
+    // an ancestor v of t whose own mask holds a token outside t's mask
+    uint32_t bad = 0;
+#pragma unroll
+    for (int v = 0; v < kMaxTok; ++v) bad |= (anc[v] & ~a) & (0u - ((a >> v) & 1u)) & (v < t ? ~0u : 0u);
+    bool ok = !live || (((a >> t) & 1u) != 0u && (a >> (t + 1)) == 0u && bad == 0u);
     const uint64_t dep = live ? (uint64_t)(__builtin_popcount(a) - 1) << (4 * t) : 0ull;
     int code = __ballot(!ok) != 0ull ? kErrInvalid : 0;
-    if (lane < p.R) {
-      const int c = sm.ctx[lane];
-      if (c < 0) ok = false;
-    }
+    if (lane < p.R && sm.ctx[lane] < 0) ok = false;
     if (__ballot(!ok) != 0ull) code = kErrInvalid;
     if (code == 0) {
       const bool cap_ok = lane >= p.R || (int64_t)sm.ctx[lane] + p.T <= (int64_t)p.cap;
@@ -2324,8 +2323,7 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   const int Nqkv = Dq + 2 * p.nkv * p.d;
   DenseSlot ring[kRing];
   if (threadIdx.x == 0) sm.zero = make_uint4(0, 0, 0, 0);
-  stage_units(p, sm);
-  if (!load_request_meta(p, sm)) return;
+  if (!load_launch_words(p, sm)) return;
 
   if constexpr ((MODE & kModeQkvOwn) != 0) {
     dense_prefetch<Epi::Qkv>(p, kSchQkv, p.cur.w_qkv, p.H, nullptr, sm, ring);
