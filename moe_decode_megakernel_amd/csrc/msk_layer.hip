@@ -2306,8 +2306,23 @@ __device__ __forceinline__ bool load_launch_words(const Params& p, Smem& sm) {
   return true;
 }
 
+// The kernel's argument block, read through an opaque pointer to the
+// kernel-argument segment. A phase that starts with its own reference loads
+// the fields it uses (scalar loads that hit the scalar cache) instead of the
+// compiler keeping every field loaded at launch start live in scalar
+// registers through the whole launch, which spills them into vector-register
+// lanes at places that shift with every change of the code.
+__device__ __forceinline__ const Params& kargs() {
+  const __attribute__((address_space(4))) Params* pp =
+      (const __attribute__((address_space(4))) Params*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(pp));
+  return *(const Params*)pp;
+}
+
 template <uint32_t MODE, int VARIANT>
-__global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
+__global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p_arg) {
+  (void)p_arg;  // read through kargs()
+  const Params& p = kargs();
   constexpr bool DEBUG = VARIANT == kDebug;
   constexpr bool TRACE = VARIANT == kTrace;
   __shared__ Smem sm;
@@ -2326,6 +2341,7 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   if (!load_launch_words(p, sm)) return;
 
   if constexpr ((MODE & kModeQkvOwn) != 0) {
+    const Params& p = kargs();
     dense_prefetch<Epi::Qkv>(p, kSchQkv, p.cur.w_qkv, p.H, nullptr, sm, ring);
     compute_inv_rms(p, p.h_in, nullptr, sm);
     fill_x_norm(p, p.h_in, p.cur.g_attn, sm);
@@ -2346,6 +2362,8 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   }
   (void)Nqkv;
 
+  {
+  const Params& p = kargs();
   // attention of the launch's layer. Workgroups without an attention item
   // publish nothing in this phase: with a speculative prefetch they arrive at
   // the barrier first and read the listed experts while the others attend.
@@ -2369,15 +2387,21 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   }
   if (!bar_wait(bar, sm)) return;
   mark(kTrAttnBar);
+  }
 
+  {
+  const Params& p = kargs();
   merge_phase<DEBUG>(p, sm, p.cur);
   mark(kTrMerge);
   bar_arrive(bar);
   if (!bar_wait_prefetch(bar, sm, [&] { dense_prefetch<Epi::OProj>(p, kSchOproj, p.cur.w_o, Dq, p.h_in, sm, ring); }))
     return;
   mark(kTrMergeBar);
+  }
 
   // output projection + residual
+  {
+  const Params& p = kargs();
   {
     fill_x_copy(p.attn, Dq, p.NT, sm);
     mark(kTrOprojFill);
@@ -2392,8 +2416,11 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   if (DEBUG && p.dbg.h1) {
     for (int i = blockIdx.x * kThreads + threadIdx.x; i < p.NT * p.H; i += gridDim.x * kThreads) p.dbg.h1[i] = p.h1[i];
   }
+  }
 
   // router + pooler (both read n2 = RMSNorm(h1))
+  {
+  const Params& p = kargs();
   {
     // the stage-dump variant has no registers to spare for batched sums
     constexpr int RB = DEBUG ? 1 : 4;
@@ -2408,8 +2435,11 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   bar_arrive(bar);
   if (!bar_wait(bar, sm)) return;
   mark(kTrRouterPoolBar);
+  }
 
   // routing (every workgroup) + experts' gate/up
+  {
+  const Params& p = kargs();
   {
     // logits first, then the first batch of the pooled activations, whose
     // loads stay in flight while the top-k runs (routing touches only the
@@ -2440,16 +2470,21 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
   bar_arrive(bar);
   if (!bar_wait(bar, sm)) return;
   mark(kTrGemm1Bar);
+  }
 
+  {
+  const Params& p = kargs();
   gemm2_phase<DEBUG>(p, sm);
   mark(kTrGemm2);
   bar_arrive(bar);
   if (!bar_wait_prefetch(bar, sm, [&] { dense_prefetch<Epi::Unpool>(p, kSchUnpool, p.cur.w_unpool, p.P, p.h1, sm, ring); }))
     return;
   mark(kTrGemm2Bar);
+  }
 
   // unpooler + residual
   {
+  const Params& p = kargs();
     const int parts = max(1, (int)gridDim.x / (p.P / 16));
     fill_x_sum(p.accpart, parts, p.P, p.NT, sm);
     mark(kTrUnpoolFill);
@@ -2466,6 +2501,7 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p) {
 
   mark(kTrUnpool);
   if constexpr ((MODE & kModeQkvNext) != 0) {
+    const Params& p = kargs();
     bar_arrive(bar);
     if (!bar_wait_prefetch(bar, sm, [&] { dense_prefetch<Epi::Qkv>(p, kSchQkv, p.nxt.w_qkv, p.H, nullptr, sm, ring); }))
       return;

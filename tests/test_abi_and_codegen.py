@@ -117,10 +117,12 @@ def test_no_scalar_cache_writes(kernel_asm):
 
 
 # Scalar registers the compiler parks in vector-register lanes (v_writelane /
-# v_readlane; no memory involved). The layer kernel keeps many kernel-argument
-# pointers live across its phases; the bound records today's level (at most
-# ~170 per instantiation) so that a change that multiplies it is noticed.
-MAX_SGPR_SPILLS = 256
+# v_readlane; no memory involved). Each phase of the layer kernel reads the
+# kernel arguments it needs afresh, so few argument fields stay live across
+# phases; the bound sits above today's level (at most ~55 per instantiation)
+# so that a change that brings the launch-long argument registers back is
+# noticed.
+MAX_SGPR_SPILLS = 80
 
 
 def test_no_scratch_spills(kernel_asm):
