@@ -11,9 +11,10 @@ that must hold bit for bit at working size.
 - The K/V bytes written to the cache equal the bf16 rounding (nearest even)
   of the kernel's own fp32 K/V projection, for every token and kv head.
 - A residual with channels at 1e4..1e5 (RMS far above 1): the QKV operand is
-  bf16 (fp32's exponent range), so the layer stays finite and within
-  tolerance, standalone and across a two-layer step (where the next layer's
-  QKV operand comes from the unpooler's epilogue).
+  the normalised residual fp16(h * inv_rms * g), at most sqrt(H) * |g| in
+  magnitude whatever the residual's scale, so the layer stays finite and
+  within tolerance, standalone and across a two-layer step (where the next
+  layer's QKV operand is built from the fp32 residual the unpooler wrote).
 - The self-timing variant gives the same bytes as the plain one.
 - Device-side request metadata: an out-of-range context length or an
   invalid token mask makes the call do nothing and report its error once.
