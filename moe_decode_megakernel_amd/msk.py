@@ -59,6 +59,9 @@ TRACE_SLOTS = ["start", "qkv_own", "qkv_own_bar", "attn_q", "attn_kv", "attn", "
                "oproj", "oproj_bar", "pool_fill", "router_pool", "router_pool_bar", "routing", "gemm1",
                "gemm1_bar", "gemm2", "gemm2_bar", "unpool_fill", "unpool", "unpool_bar", "qkv_fill", "qkv_next"]
 MAX_GRID = 256
+# tokens of one MFMA row tile: a call's requests run in passes of
+# max(1, MAX_TOKENS_PER_PASS // tokens) whole requests
+MAX_TOKENS_PER_PASS = 16
 
 
 _lib = None
