@@ -94,20 +94,20 @@ typedef enum {
 #define MSK_FLAG_KV_PREFETCH 0x4u
 
 typedef struct {
-  int32_t hidden;        /* H, multiple of 128; nq*d also a multiple of 128 */
-  int32_t n_q_heads;     /* nq */
+  int32_t hidden;        /* H: a power of two in 128..4096 */
+  int32_t n_q_heads;     /* nq: a multiple of nkv; nq * d a multiple of 128, <= 4096 */
   int32_t n_kv_heads;    /* nkv; nq / nkv <= 8 */
   int32_t head_dim;      /* d: 64 or 128 */
-  int32_t n_experts;     /* E <= 256 */
-  int32_t top_k;         /* k <= 8 */
-  int32_t pool_dim;      /* P, multiple of 128 */
-  int32_t expert_inter;  /* I, multiple of 32 */
-  int32_t n_layers;      /* layers of the step (msk_verify_step) */
-  int32_t max_tokens;    /* verify tokens per request, <= 16 */
-  int32_t max_requests;  /* <= 4 */
-  int32_t kv_capacity;   /* cache rows per (request, kv head) */
-  float rms_eps;
-  uint32_t flags;
+  int32_t n_experts;     /* E: 1..256 */
+  int32_t top_k;         /* k: 1..min(8, E) */
+  int32_t pool_dim;      /* P: a multiple of 128, <= 2048 */
+  int32_t expert_inter;  /* I: a multiple of 32, <= 1024 */
+  int32_t n_layers;      /* layers of the step (msk_verify_step), >= 1 */
+  int32_t max_tokens;    /* verify tokens per request: 1..16 */
+  int32_t max_requests;  /* 1..4 */
+  int32_t kv_capacity;   /* cache rows per (request, kv head), >= 1 */
+  float rms_eps;         /* >= 0 */
+  uint32_t flags;        /* MSK_FLAG_* bits; any other bit is rejected */
   int32_t expert_prefetch; /* 0 (off) .. min(32, n_experts): speculative expert prefetch.
                               At the start of each layer launch, the workgroups without
                               attention work rank the layer's experts by how often the
