@@ -546,8 +546,10 @@ msk::Params base_params(msk_handle h, const msk_io* io) {
   return p;
 }
 
+// Sequence numbers one launch uses: one per grid barrier, plus the router
+// sums' own arrival before the pooler's.
 int barriers_of(uint32_t mode) {
-  int n = 6;
+  int n = 7;
   if (mode & msk::kModeQkvOwn) n += 1;
   if (mode & msk::kModeQkvNext) n += 1;
   return n;

@@ -238,18 +238,23 @@ struct Barrier {
   uint32_t seq;     // sequence number of the next barrier
 };
 
-__device__ __forceinline__ void bar_arrive(Barrier& b) {
+// Arrival with sequence number seq: every store of this workgroup so far is
+// complete before its flag holds seq.
+__device__ __forceinline__ void bar_arrive_at(const Barrier& b, uint32_t seq) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0)
-    __hip_atomic_store(&b.flags[blockIdx.x], b.seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&b.flags[blockIdx.x], seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Returns false if the launch must stop (timeout or an error raised elsewhere).
-// Wave 0 alone polls every workgroup's flag (4 per lane), so the other waves
-// may have weight loads in flight without delaying the polls (vector-memory
-// counts complete in order within a wave).
-__device__ __forceinline__ bool bar_wait(Barrier& b, Smem& sm) {
+__device__ __forceinline__ void bar_arrive(Barrier& b) { bar_arrive_at(b, b.seq); }
+
+// Waits until every workgroup's flag holds at least seq. Returns false if the
+// launch must stop (timeout or an error raised elsewhere). Wave 0 alone polls
+// every workgroup's flag (4 per lane), so the other waves may have weight
+// loads in flight without delaying the polls (vector-memory counts complete
+// in order within a wave).
+__device__ __forceinline__ bool bar_wait_at(const Barrier& b, Smem& sm, uint32_t seq) {
   if (__builtin_amdgcn_readfirstlane(wave_id()) == 0) {
     const int lane = lane_id(), G = gridDim.x;
     int ok = 1;
@@ -263,7 +268,7 @@ __device__ __forceinline__ bool bar_wait(Barrier& b, Smem& sm) {
         f[j] = __hip_atomic_load(&b.flags[min(lane + 64 * j, G - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       int behind = 0;
 #pragma unroll
-      for (int j = 0; j < kMaxGrid / 64; ++j) behind += f[j] < b.seq ? 1 : 0;
+      for (int j = 0; j < kMaxGrid / 64; ++j) behind += f[j] < seq ? 1 : 0;
       if (__ballot(behind != 0) == 0) break;
       if ((polls & 63u) == 0) {
         if (__hip_atomic_load(b.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { ok = 0; break; }
@@ -277,7 +282,13 @@ __device__ __forceinline__ bool bar_wait(Barrier& b, Smem& sm) {
     if (lane == 0) sm.flag = ok;
   }
   __syncthreads();
-  const bool ok = sm.flag != 0;
+  return sm.flag != 0;
+}
+
+// The grid barrier: every workgroup has arrived with the current sequence
+// number; the next barrier uses the following one.
+__device__ __forceinline__ bool bar_wait(Barrier& b, Smem& sm) {
+  const bool ok = bar_wait_at(b, sm, b.seq);
   b.seq += 1;
   return ok;
 }
@@ -2428,12 +2439,20 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p_arg) 
     else fill_x_pool_router<false, RB>(p, sm);
     mark(kTrPoolFill);
     if (DEBUG && p.dbg.n2 && blockIdx.x == 0) dump_n2(p, sm);
+    // this workgroup's router sums are stored: announce them (sequence
+    // number bar.seq) before the pooler's work, announced with bar.seq + 1
+    bar_arrive_at(bar, bar.seq);
     EpiArgs ea{nullptr, nullptr, nullptr, p.ppart, nullptr, nullptr, nullptr};
     dense_phase<Epi::Pool>(p, kSchPool, p.cur.w_pool, p.H, p.H, ea, sm, ring);
   }
   mark(kTrRouterPool);
-  bar_arrive(bar);
-  if (!bar_wait(bar, sm)) return;
+  bar_arrive_at(bar, bar.seq + 1);
+  // top-k, gates and routing tables while the pooler finishes elsewhere:
+  // they need every workgroup's router sums only
+  if (!bar_wait_at(bar, sm, bar.seq)) return;
+  routing<DEBUG>(p, sm, blockIdx.x == 0, routing_issue(p));
+  if (!bar_wait_at(bar, sm, bar.seq + 1)) return;
+  bar.seq += 2;
   mark(kTrRouterPoolBar);
   }
 
@@ -2441,13 +2460,10 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p_arg) 
   {
   const Params& p = kargs();
   {
-    // logits first, then the first batch of the pooled activations, whose
-    // loads stay in flight while the top-k runs (routing touches only the
-    // route tables, which lie after the pooled tile in LDS)
-    const RouteLoads rl = routing_issue(p);
+    // the pooled activations (the routing tables, built before the pooler's
+    // barrier, lie after the pooled tile in LDS)
     SumLoads sl;
     fill_sum_issue(p.ppart, p.p_slices, p.P, p.NT, threadIdx.x, sl);
-    routing<DEBUG>(p, sm, blockIdx.x == 0, rl);
     fill_sum_finish(sl, p.p_slices, p.P, p.NT, threadIdx.x, sm);
     for (int i0 = threadIdx.x + kSumBatch * kThreads; i0 < kMaxTok * (p.P / 8); i0 += kSumBatch * kThreads) {
       fill_sum_issue(p.ppart, p.p_slices, p.P, p.NT, i0, sl);
