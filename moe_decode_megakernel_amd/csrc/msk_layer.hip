@@ -315,8 +315,8 @@ __device__ __forceinline__ uint4 lds_x_read(const Smem& sm, int K, int row, int 
 }
 
 // inv_rms[t] = 1/sqrt(mean(h_t^2) + eps), from per-tile partial sums (ssq
-// [ntiles][NT], summed in tile order) or, when ssq is NULL, from h directly
-// (lane j sums k = j mod 64 ascending, then pairwise halving).
+// [ntiles][NT], summed in tile order) or, when ssq is NULL, from h directly.
+// H is a power of two in 128..4096 (so H/4 is a multiple of 32).
 __device__ __forceinline__ void compute_inv_rms(const Params& p, const float* h, const float* ssq, Smem& sm) {
   const int NT = p.NT, H = p.H;
   if (!p.use_norm) {
@@ -340,12 +340,24 @@ __device__ __forceinline__ void compute_inv_rms(const Params& p, const float* h,
       if (lane == 0) sm.inv_rms[t] = rsqrtf(s / (float)H + p.eps);
     }
   } else {
-    const int lane = lane_id();
+    // lane j sums the 4-element groups j, j + 64, ... of the token's row in
+    // order (all of the row's loads in flight together), then pairwise halving
+    constexpr int kG = 4096 / 256;  // 16-byte groups per lane at the largest H
+    const int lane = lane_id(), n4 = H / 4;
     for (int t = wave_id(); t < NT; t += kWaves) {
+      const float4* hp = reinterpret_cast<const float4*>(h + (size_t)t * H);
+      float4 x[kG];
+#pragma unroll
+      for (int i = 0; i < kG; ++i) x[i] = hp[min(lane + 64 * i, n4 - 1)];
       float s = 0.0f;
-      for (int k = lane; k < H; k += 64) {
-        float v = h[(size_t)t * H + k];
-        s = fmaf(v, v, s);
+#pragma unroll
+      for (int i = 0; i < kG; ++i) {
+        if (lane + 64 * i < n4) {
+          s = fmaf(x[i].x, x[i].x, s);
+          s = fmaf(x[i].y, x[i].y, s);
+          s = fmaf(x[i].z, x[i].z, s);
+          s = fmaf(x[i].w, x[i].w, s);
+        }
       }
       for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
       if (lane == 0) sm.inv_rms[t] = rsqrtf(s / (float)H + p.eps);
