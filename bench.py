@@ -306,7 +306,9 @@ def main():
 def trace_breakdown(w, handle, h_in_t, h_out_t, msk, torch, np, dev):
     """One untimed step with the self-timing variant: per phase boundary, the
     time (us since the launch's first workgroup started) at which the slowest
-    workgroup crossed it, averaged over the launches of each layer type."""
+    workgroup crossed it, averaged over the middle launches of each layer type,
+    and for the step's first launch (which also projects its own layer's QKV)
+    and last launch (no next-layer QKV) alone."""
     L = w.n_layers
     trace = torch.zeros((L, msk.MAX_GRID, len(msk.TRACE_SLOTS)), dtype=torch.int64, device=dev)
     io = msk.make_io(w.R, w.T, [w.ctx] * w.R, h_in_t, h_out_t, trace=trace)
@@ -318,7 +320,8 @@ def trace_breakdown(w, handle, h_in_t, h_out_t, msk, torch, np, dev):
     tr = trace.cpu().numpy().astype(np.int64)
     out = {}
     groups = {"swa": [l for l in range(L) if w.windows[l] > 0 and 0 < l < L - 1],
-              "global": [l for l in range(L) if w.windows[l] <= 0 and 0 < l < L - 1]}
+              "global": [l for l in range(L) if w.windows[l] <= 0 and 0 < l < L - 1],
+              "first": [0], "last": [L - 1]}
     if L == 1:
         groups = {"layer": [0]}
     for name, ls in groups.items():
