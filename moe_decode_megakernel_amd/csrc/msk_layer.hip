@@ -340,24 +340,21 @@ __device__ __forceinline__ void compute_inv_rms(const Params& p, const float* h,
       if (lane == 0) sm.inv_rms[t] = rsqrtf(s / (float)H + p.eps);
     }
   } else {
-    // lane j sums the 4-element groups j, j + 64, ... of the token's row in
-    // order (all of the row's loads in flight together), then pairwise halving
-    constexpr int kG = 4096 / 256;  // 16-byte groups per lane at the largest H
-    const int lane = lane_id(), n4 = H / 4;
+    // lane j sums elements j, j + 64, ... of the token's row in order, then
+    // pairwise halving; the loads of half a row (at the largest H) are in
+    // flight together
+    constexpr int kE = 4096 / 64 / 2;  // elements per lane and batch at the largest H
+    const int lane = lane_id();
     for (int t = wave_id(); t < NT; t += kWaves) {
-      const float4* hp = reinterpret_cast<const float4*>(h + (size_t)t * H);
-      float4 x[kG];
-#pragma unroll
-      for (int i = 0; i < kG; ++i) x[i] = hp[min(lane + 64 * i, n4 - 1)];
+      const float* hp = h + (size_t)t * H;
       float s = 0.0f;
+      for (int b0 = 0; b0 < H; b0 += 64 * kE) {
+        float x[kE];
 #pragma unroll
-      for (int i = 0; i < kG; ++i) {
-        if (lane + 64 * i < n4) {
-          s = fmaf(x[i].x, x[i].x, s);
-          s = fmaf(x[i].y, x[i].y, s);
-          s = fmaf(x[i].z, x[i].z, s);
-          s = fmaf(x[i].w, x[i].w, s);
-        }
+        for (int i = 0; i < kE; ++i) x[i] = hp[min(b0 + lane + 64 * i, H - 1)];
+#pragma unroll
+        for (int i = 0; i < kE; ++i)
+          if (b0 + lane + 64 * i < H) s = fmaf(x[i], x[i], s);
       }
       for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
       if (lane == 0) sm.inv_rms[t] = rsqrtf(s / (float)H + p.eps);
