@@ -206,7 +206,7 @@ Layout make_layout(const msk_config* c, int G) {
     o = align_up(o + bytes, 256);
     return at;
   };
-  L.bar = take(msk::kMaxGrid * 4);
+  L.bar = take(msk::kMaxGrid * msk::kFlagStride * 4);
   L.err = take(256);
   L.zeros = take(256);
   // schedule tables: units of 4 schedules + offsets (generous bound)
@@ -331,9 +331,10 @@ msk_status create_impl(const msk_config* cfg, void* workspace, size_t bytes, boo
     delete h;
     return fail(nullptr, MSK_E_HIP, "hipMemcpy of the schedule tables failed");
   }
-  // zero the barrier word, error word and routing histogram once
-  std::vector<uint8_t> zeros(std::max<size_t>(256, 2 * (size_t)cfg->n_layers * cfg->n_experts * 4), 0);
-  if (hipMemcpy(h->ws + lay.bar, zeros.data(), 256, hipMemcpyHostToDevice) != hipSuccess ||
+  // zero the barrier flags, error word and routing histogram once
+  const size_t bar_bytes = (size_t)kMaxGrid * msk::kFlagStride * 4;
+  std::vector<uint8_t> zeros(std::max(bar_bytes, 2 * (size_t)cfg->n_layers * cfg->n_experts * 4), 0);
+  if (hipMemcpy(h->ws + lay.bar, zeros.data(), bar_bytes, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(h->ws + lay.err, zeros.data(), 256, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(h->ws + lay.zeros, zeros.data(), 256, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(h->ws + lay.hist, zeros.data(), 2 * (size_t)cfg->n_layers * cfg->n_experts * 4, hipMemcpyHostToDevice) != hipSuccess) {

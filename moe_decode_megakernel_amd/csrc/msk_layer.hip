@@ -229,11 +229,11 @@ __device__ __forceinline__ float lane_tree_sum(float acc, int n) {
 // thread publishes the barrier's sequence number in the workgroup's own flag
 // word (write-through). Waiting: wave 0 polls all flags until each reaches
 // the sequence number (bounded spin), then the workgroup meets again.
-// Flags are packed 16 per 64-byte line. No atomics, no L2 writeback or
-// invalidate. Sequence numbers grow through a call (reset at its start).
+// Each flag has a 64-byte line of its own (kFlagStride). No atomics, no L2
+// writeback or invalidate. Sequence numbers grow through a call (reset at its start).
 // ---------------------------------------------------------------------------
 struct Barrier {
-  uint32_t* flags;  // [grid] sequence numbers
+  uint32_t* flags;  // [grid][kFlagStride] sequence numbers in word 0
   int32_t* err;
   uint32_t seq;     // sequence number of the next barrier
 };
@@ -244,7 +244,7 @@ __device__ __forceinline__ void bar_arrive_at(const Barrier& b, uint32_t seq) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0)
-    __hip_atomic_store(&b.flags[blockIdx.x], seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&b.flags[blockIdx.x * kFlagStride], seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void bar_arrive(Barrier& b) { bar_arrive_at(b, b.seq); }
@@ -265,7 +265,8 @@ __device__ __forceinline__ bool bar_wait_at(const Barrier& b, Smem& sm, uint32_t
       uint32_t f[kMaxGrid / 64];
 #pragma unroll
       for (int j = 0; j < kMaxGrid / 64; ++j)
-        f[j] = __hip_atomic_load(&b.flags[min(lane + 64 * j, G - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        f[j] = __hip_atomic_load(&b.flags[min(lane + 64 * j, G - 1) * kFlagStride], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
       int behind = 0;
 #pragma unroll
       for (int j = 0; j < kMaxGrid / 64; ++j) behind += f[j] < seq ? 1 : 0;
@@ -2544,7 +2545,7 @@ __global__ void __launch_bounds__(kThreads, 1) layer_kernel(const Params p_arg) 
 // host has read the error it holds (it stays set until then, so every later
 // launch does nothing).
 __global__ void reset_kernel(uint32_t* bar, int32_t* err, int32_t clear_err) {
-  if (threadIdx.x < kMaxGrid) bar[threadIdx.x] = 0;
+  if (threadIdx.x < kMaxGrid) bar[threadIdx.x * kFlagStride] = 0;
   if (threadIdx.x == 0 && clear_err) *err = 0;
 }
 
