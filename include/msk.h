@@ -116,7 +116,8 @@ typedef struct {
                               likely experts of the previous step are prefetched) and
                               read the first expert_prefetch of them (codes and scales)
                               so that they sit in the memory-side cache when the expert
-                              phase runs. No effect on results. */
+                              phase runs. No effect on results. On MI355X at the
+                              62-layer shape, 6..10 give the shortest step. */
 } msk_config;
 
 typedef struct {
