@@ -257,6 +257,9 @@ msk_status create_impl(const msk_config* cfg, void* workspace, size_t bytes, boo
   // launch has one workgroup per compute unit
   if ((int64_t)cfg->max_requests * cfg->n_kv_heads > G)
     return fail(nullptr, MSK_E_SHAPE, "max_requests * n_kv_heads exceeds the compute units of the device");
+  // the down projection gives every 16-row tile of the pooled dim a workgroup
+  if (cfg->pool_dim / 16 > G)
+    return fail(nullptr, MSK_E_SHAPE, "pool_dim / 16 exceeds the compute units of the device");
   // the grid barrier needs every workgroup resident at once
   if (msk_layer_min_occupancy() < 1)
     return fail(nullptr, MSK_E_SHAPE, "the layer kernel does not fit one workgroup per compute unit on this device");
